@@ -1,0 +1,196 @@
+"""MI355X (gfx950) FP8 linear layer: current amax scaling, fused dual-layout
+FP8 casts, FP8 matrix-core GEMMs and a weight cache, behind a C ABI.
+
+Python side = argument marshalling over ``libfp8linear.so``.  torch is used
+for device memory and the current stream only.
+
+    quantize(x, fmt, scaling)          -> QTensor (row + col layouts, scales)
+    gemm(a, b, ...)                    -> bf16 [I, J]
+    Fp8Linear(M, K, recipe)            forward / backward with optional cache
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (E4M3, E5M2, LAYOUT_COL, LAYOUT_ROW, RECIPE_BLOCK, RECIPE_TENSOR, SCALE_1x128,
+                   SCALE_128x128, SCALE_TENSOR, Fp8Error)
+
+__all__ = ["E4M3", "E5M2", "SCALE_TENSOR", "SCALE_1x128", "SCALE_128x128", "RECIPE_TENSOR",
+           "RECIPE_BLOCK", "LAYOUT_ROW", "LAYOUT_COL", "Fp8Error", "QTensor", "quantize",
+           "gemm", "WeightCache", "Fp8Linear", "linear_workspace", "lib"]
+
+
+def lib():
+    return _lib.load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(x):
+    if not x.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    return x.device
+
+
+class QTensor:
+    """Quantized tensor buffers (torch tensors on the device) for a source of
+    shape [rows, cols] under the given scaling."""
+
+    def __init__(self, rows, cols, scaling, device, row=True, col=True):
+        self.rows, self.cols, self.scaling = rows, cols, scaling
+        u8, f32 = torch.uint8, torch.float32
+        self.q_row = torch.empty((rows, cols), dtype=u8, device=device) if row else None
+        self.q_col = torch.empty((cols, rows), dtype=u8, device=device) if col else None
+        if scaling == SCALE_TENSOR:
+            shp = (1,)
+        elif scaling == SCALE_1x128:
+            shp = (rows, cols // 128)
+        else:
+            shp = (rows // 128, cols // 128)
+        self.scale = torch.empty(shp, dtype=f32, device=device)
+        self.scale_inv = torch.empty(shp, dtype=f32, device=device)
+        if scaling == SCALE_1x128 and col:
+            self.scale_col = torch.empty((cols, rows // 128), dtype=f32, device=device)
+            self.scale_inv_col = torch.empty((cols, rows // 128), dtype=f32, device=device)
+        else:
+            self.scale_col = self.scale_inv_col = None
+        self.amax = torch.empty((1,), dtype=f32, device=device) if scaling == SCALE_TENSOR else None
+
+    def c(self):
+        return _lib.QTensorC(*(None if t is None else t.data_ptr() for t in
+                               (self.q_row, self.q_col, self.scale, self.scale_inv,
+                                self.scale_col, self.scale_inv_col, self.amax)))
+
+
+def quantize(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None):
+    """Current-scaling FP8 quantization of a bf16 [rows, cols] device tensor."""
+    L = lib()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    x = x.contiguous()
+    R, C = x.shape
+    if out is None:
+        out = QTensor(R, C, scaling, _dev(x), row=bool(layouts & LAYOUT_ROW), col=bool(layouts & LAYOUT_COL))
+    wsb = L.fp8_quantize_workspace_bytes(R, C, scaling)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
+    oc = out.c()
+    _lib.check(L.fp8_quantize(_ptr(x), R, C, fmt, scaling, layouts, ctypes.byref(oc), _ptr(ws), wsb,
+                              _stream(stream)))
+    return out
+
+
+def gemm_scale(sinv, group=0, stride_r=0, stride_kb=0):
+    """Scale descriptor of a GEMM operand; keeps a reference to the tensor so
+    the device memory stays alive as long as the descriptor does."""
+    s = _lib.GemmScaleC(sinv.data_ptr(), group, stride_r, stride_kb)
+    s._keep = sinv
+    return s
+
+
+def gemm(a, fa, sa, b, fb, sb, out=None, stream=None):
+    """C[i][j] = bf16(sum_k A[i][k] B[j][k] * scales); a [I, K], b [J, K]
+    uint8 FP8 codes; sa / sb are GemmScaleC (see gemm_scale)."""
+    L = lib()
+    I, K = a.shape
+    J, K2 = b.shape
+    if K != K2:
+        raise ValueError("contraction sizes differ")
+    if out is None:
+        out = torch.empty((I, J), dtype=torch.bfloat16, device=a.device)
+    wsb = L.fp8_gemm_workspace_bytes(I, J, K)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=a.device)
+    _lib.check(L.fp8_gemm(_ptr(a), fa, sa, _ptr(b), fb, sb, I, J, K, _ptr(out), _ptr(ws), wsb,
+                          _stream(stream)))
+    return out
+
+
+class WeightCache:
+    """Weight cache for the is_first_microbatch protocol.  Owns the device
+    buffers of the quantized weight; the library handle references them."""
+
+    def __init__(self, M, K, recipe, device):
+        self.M, self.K, self.recipe = M, K, recipe
+        self.q = QTensor(M, K, SCALE_TENSOR if recipe == RECIPE_TENSOR else SCALE_128x128, device)
+        self._qc = self.q.c()
+        h = ctypes.c_void_p()
+        _lib.check(lib().fp8_wcache_create(M, K, recipe, ctypes.byref(self._qc), ctypes.byref(h)))
+        self.handle = h
+
+    def invalidate(self):
+        _lib.check(lib().fp8_wcache_invalidate(self.handle))
+
+    @property
+    def valid(self):
+        return lib().fp8_wcache_valid(self.handle) == 1
+
+    @property
+    def fills(self):
+        return lib().fp8_wcache_fills(self.handle)
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            try:
+                lib().fp8_wcache_destroy(h)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def linear_workspace(N, K, M, recipe, device):
+    n = lib().fp8_linear_workspace_bytes(N, K, M, recipe)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device), n
+
+
+class Fp8Linear:
+    """FP8 linear layer Y = X W^T with current scaling.  Holds the buffers of
+    one forward/backward (saved X, quantized W or the cache, quantized dY)
+    for token count N, so repeated calls allocate nothing."""
+
+    def __init__(self, N, K, M, recipe=RECIPE_TENSOR, device="cuda", cache=False):
+        self.N, self.K, self.M, self.recipe = N, K, M, recipe
+        act = SCALE_TENSOR if recipe == RECIPE_TENSOR else SCALE_1x128
+        wsc = SCALE_TENSOR if recipe == RECIPE_TENSOR else SCALE_128x128
+        self.saved_x = QTensor(N, K, act, device)
+        self.dy_q = QTensor(N, M, act, device)
+        self.w_q = QTensor(M, K, wsc, device)
+        self.cache = WeightCache(M, K, recipe, device) if cache else None
+        self.ws, self.ws_bytes = linear_workspace(N, K, M, recipe, device)
+        self._sx, self._dq, self._wq = self.saved_x.c(), self.dy_q.c(), self.w_q.c()
+
+    def forward(self, x, w, y=None, is_first_microbatch=None, stream=None):
+        flag = -1 if is_first_microbatch is None else int(bool(is_first_microbatch))
+        if y is None:
+            y = torch.empty((self.N, self.M), dtype=torch.bfloat16, device=x.device)
+        cache = self.cache.handle if (self.cache is not None and flag != -1) else None
+        _lib.check(lib().fp8_linear_fwd(_ptr(x), _ptr(w), self.N, self.K, self.M, self.recipe, cache, flag,
+                                        _ptr(y), ctypes.byref(self._sx), ctypes.byref(self._wq),
+                                        _ptr(self.ws), self.ws_bytes, _stream(stream)))
+        self._last_flag = flag
+        return y
+
+    def backward(self, dy, dx=None, dw=None, need_dx=True, need_dw=True, stream=None):
+        if need_dx and dx is None:
+            dx = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dy.device)
+        if need_dw and dw is None:
+            dw = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dy.device)
+        use_cache = self.cache is not None and getattr(self, "_last_flag", -1) != -1
+        _lib.check(lib().fp8_linear_bwd(_ptr(dy), self.N, self.K, self.M, self.recipe,
+                                        ctypes.byref(self._sx), self.cache.handle if use_cache else None,
+                                        ctypes.byref(self._wq), ctypes.byref(self._dq),
+                                        _ptr(dx) if need_dx else None, _ptr(dw) if need_dw else None,
+                                        _ptr(self.ws), self.ws_bytes, _stream(stream)))
+        return dx, dw
+
+    def weight_q(self):
+        """The quantized weight the last forward used (cache or w_q)."""
+        use_cache = self.cache is not None and getattr(self, "_last_flag", -1) != -1
+        return self.cache.q if use_cache else self.w_q

@@ -1,0 +1,382 @@
+// C ABI of the FP8 linear layer: argument validation, the weight cache and
+// the composition of quantize + GEMM launches for the forward and backward
+// passes.  Every check runs before anything is enqueued.
+//
+// Data flow ("Native FP8 MLP reconstruction", implementation paragraph):
+//   forward   X -> E4M3 (row + col layouts), W -> E4M3 (row + col) unless
+//             cached, Y = GEMM(Xq_row, Wq_row)
+//   backward  dY -> E5M2 (row + col) with its own amax,
+//             dX = GEMM(dYq_row, Wq_col), dW = GEMM(dYq_col, Xq_col)
+// Weight cache (TransformerEngine issue 2852, opening post): the flag is
+// True on the first microbatch of an accumulation cycle, False on the rest
+// and None outside training.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/fp8_linear.h"
+#include "internal.hpp"
+
+struct fp8_wcache_s {
+    int64_t M, K;
+    int recipe;
+    fp8_qtensor bufs;
+    int valid;
+    int64_t fills;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fp8_status fail(fp8_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fp8_status fail(fp8_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool dim_ok(int64_t d) { return d > 0 && (d % 128) == 0 && d <= (int64_t(1) << 31); }
+
+constexpr size_t kPartialBytes = 4096;   // tensorwise amax partials (1024 words)
+
+fp8_status check_dims(const char* what, int64_t a, int64_t b) {
+    if (!dim_ok(a) || !dim_ok(b))
+        return fail(FP8_ERR_SHAPE, "%s: dimensions %lld x %lld must be positive multiples of 128", what,
+                    (long long)a, (long long)b);
+    return FP8_OK;
+}
+
+fp8_status check_ptr16(const char* what, const void* p) {
+    if (!p) return fail(FP8_ERR_NULL, "%s is NULL", what);
+    if (!aligned16(p)) return fail(FP8_ERR_ALIGN, "%s is not 16-byte aligned", what);
+    return FP8_OK;
+}
+
+fp8_status check_ptr4(const char* what, const void* p) {
+    if (!p) return fail(FP8_ERR_NULL, "%s is NULL", what);
+    if (!aligned4(p)) return fail(FP8_ERR_ALIGN, "%s is not 4-byte aligned", what);
+    return FP8_OK;
+}
+
+#define FP8_TRY(expr)                    \
+    do {                                 \
+        fp8_status _s = (expr);          \
+        if (_s != FP8_OK) return _s;     \
+    } while (0)
+
+// Validate a quantize request (no launch).
+fp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int format, int scaling, unsigned layouts,
+                          const fp8_qtensor* out) {
+    FP8_TRY(check_dims("quantize", rows, cols));
+    if (format != FP8_E4M3 && format != FP8_E5M2) return fail(FP8_ERR_ENUM, "unknown format %d", format);
+    if (scaling < FP8_SCALE_TENSOR || scaling > FP8_SCALE_BLOCK_128x128)
+        return fail(FP8_ERR_ENUM, "unknown scaling %d", scaling);
+    if (layouts == 0 || (layouts & ~3u) != 0) return fail(FP8_ERR_ENUM, "bad layout mask %u", layouts);
+    FP8_TRY(check_ptr16("x", x));
+    if (!out) return fail(FP8_ERR_NULL, "output descriptor is NULL");
+    if (layouts & FP8_LAYOUT_ROW) FP8_TRY(check_ptr16("q_row", out->q_row));
+    if (layouts & FP8_LAYOUT_COL) FP8_TRY(check_ptr16("q_col", out->q_col));
+    const bool row_scales = scaling != FP8_SCALE_BLOCK_1x128 || (layouts & FP8_LAYOUT_ROW);
+    if (row_scales) {
+        FP8_TRY(check_ptr4("scale", out->scale));
+        FP8_TRY(check_ptr4("scale_inv", out->scale_inv));
+    }
+    if (scaling == FP8_SCALE_BLOCK_1x128 && (layouts & FP8_LAYOUT_COL)) {
+        FP8_TRY(check_ptr4("scale_col", out->scale_col));
+        FP8_TRY(check_ptr4("scale_inv_col", out->scale_inv_col));
+    }
+    if (out->amax && !aligned4(out->amax)) return fail(FP8_ERR_ALIGN, "amax is not 4-byte aligned");
+    return FP8_OK;
+}
+
+fp8_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FP8_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return FP8_OK;
+}
+
+fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, int scaling, unsigned layouts,
+                       const fp8_qtensor* out, void* ws, hipStream_t st) {
+    fp8k::QuantizeLaunch q;
+    q.x = x;
+    q.rows = rows;
+    q.cols = cols;
+    q.format = format;
+    q.scaling = scaling;
+    q.q_row = (layouts & FP8_LAYOUT_ROW) ? out->q_row : nullptr;
+    q.q_col = (layouts & FP8_LAYOUT_COL) ? out->q_col : nullptr;
+    q.scale = out->scale;
+    q.scale_inv = out->scale_inv;
+    q.scale_col = out->scale_col;
+    q.scale_inv_col = out->scale_inv_col;
+    q.amax = scaling == FP8_SCALE_TENSOR ? out->amax : nullptr;
+    q.partial = static_cast<uint32_t*>(ws);
+    return hip_status(fp8k::launch_quantize(q, st), "quantize launch");
+}
+
+fp8k::GemmScale tensor_scale(const float* sinv) { return fp8k::GemmScale{sinv, 0, 0, 0}; }
+fp8k::GemmScale block_scale(const float* sinv, int64_t group, int64_t sr, int64_t sk) {
+    return fp8k::GemmScale{sinv, group, sr, sk};
+}
+
+fp8_status do_gemm(const void* a, int fa, fp8k::GemmScale sa, const void* b, int fb, fp8k::GemmScale sb, int64_t I,
+                   int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, hipStream_t st) {
+    fp8k::GemmLaunch g;
+    g.a = a;
+    g.fa = fa;
+    g.sa = sa;
+    g.b = b;
+    g.fb = fb;
+    g.sb = sb;
+    g.I = I;
+    g.J = J;
+    g.K = K;
+    g.c = c;
+    g.ws = ws;
+    g.ws_bytes = ws_bytes;
+    return hip_status(fp8k::launch_gemm(g, st), "gemm launch");
+}
+
+size_t linear_gemm_ws(int64_t N, int64_t K, int64_t M) {
+    size_t a = fp8k::gemm_ws_bytes(N, M, K);   // fprop
+    size_t b = fp8k::gemm_ws_bytes(N, K, M);   // dgrad
+    size_t c = fp8k::gemm_ws_bytes(M, K, N);   // wgrad
+    size_t m = a > b ? a : b;
+    return m > c ? m : c;
+}
+
+fp8_status check_weight_q(const fp8_qtensor* w, int recipe, bool need_row, bool need_col) {
+    if (!w) return fail(FP8_ERR_NULL, "quantized weight descriptor is NULL");
+    if (need_row) FP8_TRY(check_ptr16("w_q.q_row", w->q_row));
+    if (need_col) FP8_TRY(check_ptr16("w_q.q_col", w->q_col));
+    FP8_TRY(check_ptr4("w_q.scale", w->scale));
+    FP8_TRY(check_ptr4("w_q.scale_inv", w->scale_inv));
+    (void)recipe;
+    return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(fp8_status s) {
+    switch (s) {
+        case FP8_OK: return "FP8_OK";
+        case FP8_ERR_NULL: return "FP8_ERR_NULL";
+        case FP8_ERR_SHAPE: return "FP8_ERR_SHAPE";
+        case FP8_ERR_ALIGN: return "FP8_ERR_ALIGN";
+        case FP8_ERR_ENUM: return "FP8_ERR_ENUM";
+        case FP8_ERR_WORKSPACE: return "FP8_ERR_WORKSPACE";
+        case FP8_ERR_CACHE_EMPTY: return "FP8_ERR_CACHE_EMPTY";
+        case FP8_ERR_CACHE_MISMATCH: return "FP8_ERR_CACHE_MISMATCH";
+        case FP8_ERR_HIP: return "FP8_ERR_HIP";
+        case FP8_ERR_UNIMPLEMENTED: return "FP8_ERR_UNIMPLEMENTED";
+    }
+    return "FP8_ERR_UNKNOWN";
+}
+
+const char* fp8_last_error(void) { return g_last_error.c_str(); }
+
+const char* fp8_version(void) { return "fp8linear-gfx950 0.1"; }
+
+size_t fp8_quantize_workspace_bytes(int64_t rows, int64_t cols, fp8_scaling scaling) {
+    (void)rows;
+    (void)cols;
+    return scaling == FP8_SCALE_TENSOR ? kPartialBytes : 0;
+}
+
+fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_format format, fp8_scaling scaling,
+                        unsigned layouts, const fp8_qtensor* out, void* ws, size_t ws_bytes, void* stream) {
+    FP8_TRY(check_quantize(x, rows, cols, format, scaling, layouts, out));
+    const size_t need = fp8_quantize_workspace_bytes(rows, cols, scaling);
+    if (need) {
+        if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+        FP8_TRY(check_ptr16("ws", ws));
+    }
+    return do_quantize(x, rows, cols, format, scaling, layouts, out, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t fp8_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K) { return fp8k::gemm_ws_bytes(I, J, K); }
+
+fp8_status fp8_gemm(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb, fp8_gemm_scale sb,
+                    int64_t I, int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, void* stream) {
+    FP8_TRY(check_dims("gemm I x J", I, J));
+    FP8_TRY(check_dims("gemm K", K, 128));
+    if ((fa != FP8_E4M3 && fa != FP8_E5M2) || (fb != FP8_E4M3 && fb != FP8_E5M2))
+        return fail(FP8_ERR_ENUM, "unknown operand format");
+    FP8_TRY(check_ptr16("a", a));
+    FP8_TRY(check_ptr16("b", b));
+    FP8_TRY(check_ptr16("c", c));
+    FP8_TRY(check_ptr4("scale_a", sa.scale_inv));
+    FP8_TRY(check_ptr4("scale_b", sb.scale_inv));
+    if ((sa.group == 0) != (sb.group == 0))
+        return fail(FP8_ERR_ENUM, "both operands must be tensorwise or both block-scaled");
+    if (sa.group != 0 && sa.group != 1 && sa.group != 128) return fail(FP8_ERR_ENUM, "scale_a.group must be 0, 1 or 128");
+    if (sb.group != 0 && sb.group != 1 && sb.group != 128) return fail(FP8_ERR_ENUM, "scale_b.group must be 0, 1 or 128");
+    const size_t need = fp8k::gemm_ws_bytes(I, J, K);
+    if (need) {
+        if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+        FP8_TRY(check_ptr16("ws", ws));
+    }
+    return do_gemm(a, fa, fp8k::GemmScale{sa.scale_inv, sa.group, sa.stride_r, sa.stride_kb}, b, fb,
+                   fp8k::GemmScale{sb.scale_inv, sb.group, sb.stride_r, sb.stride_kb}, I, J, K, c, ws, ws_bytes,
+                   static_cast<hipStream_t>(stream));
+}
+
+fp8_status fp8_wcache_create(int64_t M, int64_t K, fp8_recipe recipe, const fp8_qtensor* bufs, fp8_wcache* out) {
+    if (!out) return fail(FP8_ERR_NULL, "output handle pointer is NULL");
+    FP8_TRY(check_dims("weight cache", M, K));
+    if (recipe != FP8_RECIPE_TENSOR && recipe != FP8_RECIPE_BLOCK) return fail(FP8_ERR_ENUM, "unknown recipe %d", recipe);
+    FP8_TRY(check_weight_q(bufs, recipe, true, true));
+    fp8_wcache h = static_cast<fp8_wcache>(std::calloc(1, sizeof(fp8_wcache_s)));
+    if (!h) return fail(FP8_ERR_NULL, "out of host memory");
+    h->M = M;
+    h->K = K;
+    h->recipe = recipe;
+    h->bufs = *bufs;
+    h->valid = 0;
+    h->fills = 0;
+    *out = h;
+    return FP8_OK;
+}
+
+fp8_status fp8_wcache_invalidate(fp8_wcache h) {
+    if (!h) return fail(FP8_ERR_NULL, "cache handle is NULL");
+    h->valid = 0;
+    return FP8_OK;
+}
+
+int fp8_wcache_valid(fp8_wcache h) { return h ? h->valid : -1; }
+int64_t fp8_wcache_fills(fp8_wcache h) { return h ? h->fills : -1; }
+void fp8_wcache_destroy(fp8_wcache h) { std::free(h); }
+
+size_t fp8_linear_workspace_bytes(int64_t N, int64_t K, int64_t M, fp8_recipe recipe) {
+    (void)recipe;
+    return kPartialBytes + linear_gemm_ws(N, K, M);
+}
+
+static fp8_status check_linear_common(int64_t N, int64_t K, int64_t M, int recipe, void* ws, size_t ws_bytes) {
+    FP8_TRY(check_dims("linear N x K", N, K));
+    FP8_TRY(check_dims("linear M", M, 128));
+    if (recipe != FP8_RECIPE_TENSOR && recipe != FP8_RECIPE_BLOCK) return fail(FP8_ERR_ENUM, "unknown recipe %d", recipe);
+    const size_t need = fp8_linear_workspace_bytes(N, K, M, static_cast<fp8_recipe>(recipe));
+    if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    FP8_TRY(check_ptr16("ws", ws));
+    return FP8_OK;
+}
+
+static fp8_status check_cache(fp8_wcache cache, int64_t M, int64_t K, int recipe) {
+    if (!cache) return fail(FP8_ERR_NULL, "cache handle is NULL");
+    if (cache->M != M || cache->K != K || cache->recipe != recipe)
+        return fail(FP8_ERR_CACHE_MISMATCH, "cache holds %lld x %lld recipe %d, call has %lld x %lld recipe %d",
+                    (long long)cache->M, (long long)cache->K, cache->recipe, (long long)M, (long long)K, recipe);
+    return FP8_OK;
+}
+
+fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                          fp8_wcache cache, int flag, void* y, const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
+                          void* ws, size_t ws_bytes, void* stream) {
+    FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes));
+    if (flag != -1 && flag != 0 && flag != 1) return fail(FP8_ERR_ENUM, "is_first_microbatch must be -1, 0 or 1");
+    FP8_TRY(check_ptr16("x", x));
+    FP8_TRY(check_ptr16("y", y));
+    const int act = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
+    const int wsc = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_128x128 : FP8_SCALE_TENSOR;
+    FP8_TRY(check_quantize(x, N, K, FP8_E4M3, act, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x));
+    const fp8_qtensor* wq = nullptr;
+    if (flag == -1) {
+        FP8_TRY(check_weight_q(w_q, recipe, true, true));
+        FP8_TRY(check_quantize(w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, w_q));
+        wq = w_q;
+    } else {
+        FP8_TRY(check_cache(cache, M, K, recipe));
+        if (flag == 1) {
+            FP8_TRY(check_quantize(w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, &cache->bufs));
+        } else if (!cache->valid) {
+            return fail(FP8_ERR_CACHE_EMPTY, "is_first_microbatch=False on an empty weight cache");
+        }
+        wq = &cache->bufs;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    void* gws = wsb + kPartialBytes;
+    const size_t gws_bytes = ws_bytes - kPartialBytes;
+    if (flag != 0) {
+        FP8_TRY(do_quantize(w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, wq, ws, st));
+        if (flag == 1) {
+            cache->valid = 1;
+            cache->fills++;
+        }
+    }
+    FP8_TRY(do_quantize(x, N, K, FP8_E4M3, act, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x, ws, st));
+    if (recipe == FP8_RECIPE_TENSOR)
+        return do_gemm(saved_x->q_row, FP8_E4M3, tensor_scale(saved_x->scale_inv), wq->q_row, FP8_E4M3,
+                       tensor_scale(wq->scale_inv), N, M, K, y, gws, gws_bytes, st);
+    return do_gemm(saved_x->q_row, FP8_E4M3, block_scale(saved_x->scale_inv, 1, K / 128, 1), wq->q_row, FP8_E4M3,
+                   block_scale(wq->scale_inv, 128, K / 128, 1), N, M, K, y, gws, gws_bytes, st);
+}
+
+fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                          const fp8_qtensor* saved_x, fp8_wcache cache, const fp8_qtensor* w_q,
+                          const fp8_qtensor* dy_q, void* dx, void* dw, void* ws, size_t ws_bytes, void* stream) {
+    FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes));
+    FP8_TRY(check_ptr16("dy", dy));
+    if (!dx && !dw) return fail(FP8_ERR_NULL, "both dx and dw are NULL: nothing to compute");
+    if (dx) FP8_TRY(check_ptr16("dx", dx));
+    if (dw) FP8_TRY(check_ptr16("dw", dw));
+    const int act = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
+    const unsigned lay = (dx ? FP8_LAYOUT_ROW : 0u) | (dw ? FP8_LAYOUT_COL : 0u);
+    FP8_TRY(check_quantize(dy, N, M, FP8_E5M2, act, lay, dy_q));
+    const fp8_qtensor* wq = nullptr;
+    if (dx) {
+        if (cache) {
+            FP8_TRY(check_cache(cache, M, K, recipe));
+            if (!cache->valid) return fail(FP8_ERR_CACHE_EMPTY, "backward with an empty weight cache");
+            wq = &cache->bufs;
+        } else {
+            FP8_TRY(check_weight_q(w_q, recipe, false, true));
+            wq = w_q;
+        }
+    }
+    if (dw) {
+        if (!saved_x) return fail(FP8_ERR_NULL, "saved_x is NULL");
+        FP8_TRY(check_ptr16("saved_x.q_col", saved_x->q_col));
+        if (recipe == FP8_RECIPE_BLOCK) FP8_TRY(check_ptr4("saved_x.scale_inv_col", saved_x->scale_inv_col));
+        else FP8_TRY(check_ptr4("saved_x.scale_inv", saved_x->scale_inv));
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    void* gws = wsb + kPartialBytes;
+    const size_t gws_bytes = ws_bytes - kPartialBytes;
+    FP8_TRY(do_quantize(dy, N, M, FP8_E5M2, act, lay, dy_q, ws, st));
+    if (dx) {
+        if (recipe == FP8_RECIPE_TENSOR)
+            FP8_TRY(do_gemm(dy_q->q_row, FP8_E5M2, tensor_scale(dy_q->scale_inv), wq->q_col, FP8_E4M3,
+                            tensor_scale(wq->scale_inv), N, K, M, dx, gws, gws_bytes, st));
+        else
+            FP8_TRY(do_gemm(dy_q->q_row, FP8_E5M2, block_scale(dy_q->scale_inv, 1, M / 128, 1), wq->q_col, FP8_E4M3,
+                            block_scale(wq->scale_inv, 128, 1, K / 128), N, K, M, dx, gws, gws_bytes, st));
+    }
+    if (dw) {
+        if (recipe == FP8_RECIPE_TENSOR)
+            FP8_TRY(do_gemm(dy_q->q_col, FP8_E5M2, tensor_scale(dy_q->scale_inv), saved_x->q_col, FP8_E4M3,
+                            tensor_scale(saved_x->scale_inv), M, K, N, dw, gws, gws_bytes, st));
+        else
+            FP8_TRY(do_gemm(dy_q->q_col, FP8_E5M2, block_scale(dy_q->scale_inv_col, 1, N / 128, 1), saved_x->q_col,
+                            FP8_E4M3, block_scale(saved_x->scale_inv_col, 1, N / 128, 1), M, K, N, dw, gws, gws_bytes,
+                            st));
+    }
+    return FP8_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8k {
+
+constexpr int kMaxAmaxPartials = 1024;
+
+struct QuantizeLaunch {
+    const void* x;      // [rows, cols] bf16
+    int64_t rows, cols;
+    int format;         // 0 E4M3, 1 E5M2
+    int scaling;        // 0 tensor, 1 1x128, 2 128x128
+    void* q_row;        // may be null
+    void* q_col;        // may be null
+    float* scale;
+    float* scale_inv;
+    float* scale_col;
+    float* scale_inv_col;
+    float* amax;        // optional
+    uint32_t* partial;  // tensor: kMaxAmaxPartials words of scratch
+};
+
+int amax_partial_count(int64_t numel);
+hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream);
+
+struct GemmScale {
+    const float* sinv;
+    int64_t group;      // 0 tensorwise, else rows per scale group (1 or 128)
+    int64_t stride_r;
+    int64_t stride_kb;
+};
+
+struct GemmLaunch {
+    const void* a;      // [I, K] FP8
+    int fa;
+    GemmScale sa;
+    const void* b;      // [J, K] FP8
+    int fb;
+    GemmScale sb;
+    int64_t I, J, K;
+    void* c;            // [I, J] bf16
+    void* ws;           // split-K partials
+    size_t ws_bytes;
+};
+
+// Split-K factor the GEMM launcher will use for this shape (1 = none) and
+// the workspace bytes that needs.
+int gemm_splits(int64_t I, int64_t J, int64_t K, bool block);
+size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K);
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
+
+}  // namespace fp8k

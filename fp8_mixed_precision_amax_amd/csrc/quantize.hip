@@ -1,0 +1,289 @@
+// Current-scaling FP8 quantizers for gfx950.
+//
+// Method ("Native FP8 MLP reconstruction", implementation paragraph): the
+// scale of every tensor comes from its current amax, and one fused cast
+// emits the ordinary and the transposed FP8 layouts.  Block scaling follows
+// the Float8BlockScaling recipe named in TransformerEngine issue 2852
+// (opening post): blockwise amax, no amax history.
+//
+// Kernels
+//   amax_partial_kernel   tensorwise amax, pass 1: grid-stride 16-byte loads,
+//                         packed 16-bit max on bf16 magnitude bits, wave and
+//                         workgroup reduction, one partial max per workgroup.
+//   cast_kernel<FMT,MODE> one wave per 128x128 tile, no LDS: lane (rb, cb)
+//                         owns rows rb*32..+31, columns cb*8..+7 of the tile
+//                         (16-byte coalesced loads, 256 contiguous bytes per
+//                         row per instruction); codes from the hardware
+//                         converters (v_cvt_pk_fp8/bf8_f32, clamped first);
+//                         the transposed layout comes from in-register 4x4
+//                         byte transposes (v_perm_b32) and is written with
+//                         16-byte stores.
+//     MODE 0 tensorwise: the scale is rebuilt in each wave from the amax
+//            partials of pass 1 (so the cast needs no separate launch).
+//     MODE 1 1x128 blocks: row blocks reduce over the 16 lanes of a DPP row;
+//            column blocks reduce the lane's 32 rows, then across the 4 lane
+//            rows with two xor shuffles.  The column layout is requantized
+//            with the column-block scales.
+//     MODE 2 128x128 blocks: one scale per tile (wave-wide reduction).
+#include "device.hpp"
+#include "internal.hpp"
+
+namespace fp8k {
+
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxUnroll = 4;
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                                    uint32_t* __restrict__ partial) {
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    for (; i + (kAmaxUnroll - 1) * stride < n16; i += kAmaxUnroll * stride) {
+        uint4 v[kAmaxUnroll];
+#pragma unroll
+        for (int u = 0; u < kAmaxUnroll; u++) v[u] = ld_nt16(x + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kAmaxUnroll; u++)
+            m = pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v[u].x), mag2(v[u].y)), pkmax_u16(mag2(v[u].z), mag2(v[u].w))));
+    }
+    for (; i < n16; i += stride) {
+        uint4 v = x[i];
+        m = pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v.x), mag2(v.y)), pkmax_u16(mag2(v.z), mag2(v.w))));
+    }
+    m = wave_max_u32(hmax_u16(m));
+    __shared__ uint32_t red[kAmaxThreads / 64];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = red[0];
+        for (int w = 1; w < kAmaxThreads / 64; w++) r = r > red[w] ? r : red[w];
+        partial[blockIdx.x] = r;
+    }
+}
+
+struct CastArgs {
+    const uint16_t* x;  // [R, C] bf16
+    int64_t R, C;
+    uint8_t* q_row;     // [R, C] or null
+    uint8_t* q_col;     // [C, R] or null
+    float* scale;       // tensor: [1]; 1x128: [R, C/128]; 128x128: [R/128, C/128]
+    float* scale_inv;
+    float* scale_col;   // 1x128 only: [C, R/128]
+    float* scale_inv_col;
+    float* amax_out;    // tensor only, optional
+    const uint32_t* partial;  // tensor only: amax partials of pass 1
+    int npartial;
+};
+
+template <int FMT, int MODE>
+__global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t tiles_c = a.C >> 7;
+    const int64_t ntiles = (a.R >> 7) * tiles_c;
+    const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
+    if (tile >= ntiles) return;
+    const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
+    const int rb = lane >> 4, cb = lane & 15;
+    const int64_t row0 = tr * 128 + rb * 32;   // first of this lane's 32 rows
+    const int64_t col0 = tc * 128 + cb * 8;    // first of this lane's 8 columns
+
+    // ---- load 32 rows x 8 bf16 ------------------------------------------
+    uint4 v[32];
+    const uint16_t* src = a.x + row0 * a.C + col0;
+#pragma unroll
+    for (int i = 0; i < 32; i++) v[i] = ld_nt16(src + i * a.C);
+
+    // ---- scales ---------------------------------------------------------
+    float s_tile = 1.0f;          // MODE 0 and 2
+    bool nan_any = false;
+    if constexpr (MODE == 0) {
+        uint32_t m = 0;
+        for (int p = lane; p < a.npartial; p += 64) m = m > a.partial[p] ? m : a.partial[p];
+        m = wave_max_u32(m);
+        float si;
+        scale_from_amax_bits<FMT>(m, s_tile, si);
+        nan_any = m > 0x7F80u;
+        if (tile == 0 && lane == 0) {
+            a.scale[0] = s_tile;
+            a.scale_inv[0] = si;
+            if (a.amax_out) a.amax_out[0] = m > 0x7F80u ? __uint_as_float(0x7FC00000u) : __uint_as_float(m << 16);
+        }
+    } else if constexpr (MODE == 2) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 32; i++)
+            m = pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v[i].x), mag2(v[i].y)), pkmax_u16(mag2(v[i].z), mag2(v[i].w))));
+        m = wave_max_u32(hmax_u16(m));
+        float si;
+        scale_from_amax_bits<FMT>(m, s_tile, si);
+        nan_any = m > 0x7F80u;
+        if (lane == 0) {
+            a.scale[tr * tiles_c + tc] = s_tile;
+            a.scale_inv[tr * tiles_c + tc] = si;
+        }
+    }
+
+    if constexpr (MODE == 0 || MODE == 2) {
+        // One scale for the whole tile: the column layout is the transpose
+        // of the row layout.
+        uint2 code[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            code[i] = enc8<FMT>(v[i], s_tile);
+            if (nan_any) code[i] = patch_nan8(v[i], code[i]);
+        }
+        if (a.q_row) {
+#pragma unroll
+            for (int i = 0; i < 32; i++)
+                st_nt8(a.q_row + (row0 + i) * a.C + col0, code[i]);
+        }
+        if (a.q_col) {
+            uint32_t t[8][8];   // t[column j][row group h]
+#pragma unroll
+            for (int h = 0; h < 8; h++) {
+                transpose4x4(code[4 * h].x, code[4 * h + 1].x, code[4 * h + 2].x, code[4 * h + 3].x,
+                             t[0][h], t[1][h], t[2][h], t[3][h]);
+                transpose4x4(code[4 * h].y, code[4 * h + 1].y, code[4 * h + 2].y, code[4 * h + 3].y,
+                             t[4][h], t[5][h], t[6][h], t[7][h]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                uint8_t* dst = a.q_col + (col0 + j) * a.R + row0;
+                st_nt16(dst, make_uint4(t[j][0], t[j][1], t[j][2], t[j][3]));
+                st_nt16(dst + 16, make_uint4(t[j][4], t[j][5], t[j][6], t[j][7]));
+            }
+        }
+    } else {
+        // ---- MODE 1: 1x128 row blocks and 128x1 column blocks ------------
+        const int64_t cblocks = a.C >> 7, rblocks = a.R >> 7;
+        if (a.q_row) {
+            // row maxima: two rows per packed dword, reduced over the DPP row
+            uint32_t rm[16];
+#pragma unroll
+            for (int p = 0; p < 16; p++) {
+                uint32_t m0 = pkmax_u16(pkmax_u16(mag2(v[2 * p].x), mag2(v[2 * p].y)), pkmax_u16(mag2(v[2 * p].z), mag2(v[2 * p].w)));
+                uint32_t m1 = pkmax_u16(pkmax_u16(mag2(v[2 * p + 1].x), mag2(v[2 * p + 1].y)), pkmax_u16(mag2(v[2 * p + 1].z), mag2(v[2 * p + 1].w)));
+                rm[p] = hmax_u16(m0) | (hmax_u16(m1) << 16);
+                rm[p] = row16_pkmax(rm[p]);
+            }
+#pragma unroll
+            for (int p = 0; p < 16; p++) {
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const int i = 2 * p + h;
+                    const uint32_t m = h ? (rm[p] >> 16) : (rm[p] & 0xFFFFu);
+                    float s, si;
+                    scale_from_amax_bits<FMT>(m, s, si);
+                    uint2 c = enc8<FMT>(v[i], s);
+                    if (m > 0x7F80u) c = patch_nan8(v[i], c);
+                    st_nt8(a.q_row + (row0 + i) * a.C + col0, c);
+                    if ((i >> 1) == cb) {   // lane cb writes rows 2cb, 2cb+1
+                        a.scale[(row0 + i) * cblocks + tc] = s;
+                        a.scale_inv[(row0 + i) * cblocks + tc] = si;
+                    }
+                }
+            }
+        }
+        if (a.q_col) {
+            // column maxima over the lane's 32 rows, then over the 4 lane rows
+            uint32_t cm[4];
+            cm[0] = mag2(v[0].x); cm[1] = mag2(v[0].y); cm[2] = mag2(v[0].z); cm[3] = mag2(v[0].w);
+#pragma unroll
+            for (int i = 1; i < 32; i++) {
+                cm[0] = pkmax_u16(cm[0], mag2(v[i].x));
+                cm[1] = pkmax_u16(cm[1], mag2(v[i].y));
+                cm[2] = pkmax_u16(cm[2], mag2(v[i].z));
+                cm[3] = pkmax_u16(cm[3], mag2(v[i].w));
+            }
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                cm[g] = pkmax_u16(cm[g], (uint32_t)__shfl_xor((int)cm[g], 16, 64));
+                cm[g] = pkmax_u16(cm[g], (uint32_t)__shfl_xor((int)cm[g], 32, 64));
+            }
+            float sc[8];
+            bool nan_col = false;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint32_t m = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
+                float si;
+                scale_from_amax_bits<FMT>(m, sc[j], si);
+                nan_col |= m > 0x7F80u;
+                if (rb == 0) {
+                    a.scale_col[(col0 + j) * rblocks + tr] = sc[j];
+                    a.scale_inv_col[(col0 + j) * rblocks + tr] = si;
+                }
+            }
+            uint32_t t[8][8];
+#pragma unroll
+            for (int h = 0; h < 8; h++) {
+                uint2 c0 = enc8_cols<FMT>(v[4 * h], sc);
+                uint2 c1 = enc8_cols<FMT>(v[4 * h + 1], sc);
+                uint2 c2 = enc8_cols<FMT>(v[4 * h + 2], sc);
+                uint2 c3 = enc8_cols<FMT>(v[4 * h + 3], sc);
+                if (nan_col) {
+                    c0 = patch_nan8(v[4 * h], c0);
+                    c1 = patch_nan8(v[4 * h + 1], c1);
+                    c2 = patch_nan8(v[4 * h + 2], c2);
+                    c3 = patch_nan8(v[4 * h + 3], c3);
+                }
+                transpose4x4(c0.x, c1.x, c2.x, c3.x, t[0][h], t[1][h], t[2][h], t[3][h]);
+                transpose4x4(c0.y, c1.y, c2.y, c3.y, t[4][h], t[5][h], t[6][h], t[7][h]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                uint8_t* dst = a.q_col + (col0 + j) * a.R + row0;
+                st_nt16(dst, make_uint4(t[j][0], t[j][1], t[j][2], t[j][3]));
+                st_nt16(dst + 16, make_uint4(t[j][4], t[j][5], t[j][6], t[j][7]));
+            }
+        }
+    }
+}
+
+int amax_partial_count(int64_t numel) {
+    const int64_t n16 = numel / 8;
+    int64_t g = (n16 + (int64_t)kAmaxThreads * kAmaxUnroll * 8 - 1) / ((int64_t)kAmaxThreads * kAmaxUnroll * 8);
+    if (g < 1) g = 1;
+    if (g > kMaxAmaxPartials) g = kMaxAmaxPartials;
+    return (int)g;
+}
+
+hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
+    CastArgs a;
+    a.x = static_cast<const uint16_t*>(q.x);
+    a.R = q.rows;
+    a.C = q.cols;
+    a.q_row = static_cast<uint8_t*>(q.q_row);
+    a.q_col = static_cast<uint8_t*>(q.q_col);
+    a.scale = q.scale;
+    a.scale_inv = q.scale_inv;
+    a.scale_col = q.scale_col;
+    a.scale_inv_col = q.scale_inv_col;
+    a.amax_out = q.amax;
+    a.partial = q.partial;
+    a.npartial = 0;
+    if (q.scaling == 0) {
+        const int g = amax_partial_count(q.rows * q.cols);
+        a.npartial = g;
+        hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(kAmaxThreads), 0, stream,
+                           static_cast<const uint4*>(q.x), q.rows * q.cols / 8, q.partial);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t ntiles = (q.rows / 128) * (q.cols / 128);
+    const dim3 grid((unsigned)((ntiles + 3) / 4));
+#define FP8K_CAST(F, M) hipLaunchKernelGGL((cast_kernel<F, M>), grid, dim3(256), 0, stream, a)
+    if (q.format == 0) {
+        if (q.scaling == 0) FP8K_CAST(0, 0);
+        else if (q.scaling == 1) FP8K_CAST(0, 1);
+        else FP8K_CAST(0, 2);
+    } else {
+        if (q.scaling == 0) FP8K_CAST(1, 0);
+        else if (q.scaling == 1) FP8K_CAST(1, 1);
+        else FP8K_CAST(1, 2);
+    }
+#undef FP8K_CAST
+    return hipGetLastError();
+}
+
+}  // namespace fp8k

@@ -1,0 +1,240 @@
+/*
+ * fp8_linear.h -- C ABI of the MI355X (gfx950) FP8 linear layer.
+ *
+ * The library computes the forward and backward pass of a linear layer in
+ * FP8 with current scaling, as described in "Native FP8 MLP reconstruction"
+ * (rstation.ai, implementation paragraph): a current amax sets each tensor's
+ * scale on every call, inputs and weights are cast to E4M3 and incoming
+ * gradients to E5M2, one fused cast writes both the ordinary and the
+ * transposed layout, the three GEMMs (Y = X W^T, dX = dY W, dW = dY^T X)
+ * accumulate in full fp32 precision (no fast accumulation) and write BF16,
+ * scales are treated as constants in the backward pass, and the backward
+ * pass reuses the forward-rounded X and W while rounding the incoming
+ * gradient on its own.  A block-scaled recipe (the Float8BlockScaling recipe
+ * of TransformerEngine issue 2852, opening post) quantizes activations and
+ * gradients in 1x128 blocks and weights in 128x128 blocks.  A weight cache
+ * implements the is_first_microbatch protocol of the same issue (opening
+ * post and the user's description of their flag injection): True quantizes
+ * the weight and keeps it, False reuses the kept copy, None (-1) neither
+ * reads nor writes it; for these non-delayed recipes the cached and
+ * recomputed results are bitwise identical (maintainer reply in the issue).
+ *
+ * Conventions
+ *  - Shapes follow nn.Linear: X [N, K], W [M, K] (out x in), Y [N, M],
+ *    dY [N, M], dX [N, K], dW [M, K].  Every dimension must be a positive
+ *    multiple of 128 (FP8_ERR_SHAPE otherwise).
+ *  - Every tensor argument is a DEVICE pointer owned by the caller, row-major
+ *    and 16-byte aligned (FP8_ERR_ALIGN otherwise).  bf16 tensors are raw
+ *    16-bit patterns; FP8 tensors are one OCP code per byte (E4M3 "FN":
+ *    max 448, NaN 0x7F; E5M2: max 57344).
+ *  - The library allocates no device memory.  Functions that need scratch
+ *    take (ws, ws_bytes); the needed size comes from the *_workspace_bytes
+ *    queries.  Workspace contents need no initialisation and are not
+ *    preserved between calls.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *    All device work is enqueued on it asynchronously; no call synchronises
+ *    the host.  Calls that share a workspace or a cache must be ordered on
+ *    one stream (or by the caller).
+ *  - Errors: every argument, shape, alignment and enum check happens before
+ *    anything is enqueued, and a failed check leaves every output untouched.
+ *    A failed kernel launch returns FP8_ERR_HIP.  fp8_last_error() gives a
+ *    message for the calling thread's last failure.  Non-finite inputs are
+ *    not errors: NaN encodes to 0x7F, +-Inf saturates to +-max, and a
+ *    non-finite or zero amax gives scale 1.
+ *
+ * Scale semantics (per tensor, or per block)
+ *    amax      = max |x| over the tensor / block (NaN if any NaN)
+ *    scale     = FMAX / amax (fp32 division; 1 if amax is 0, Inf or NaN;
+ *                FLT_MAX if the division overflows)
+ *    scale_inv = 1 / scale (fp32 division), the dequantisation factor
+ *    q         = encode_rne_saturating(fl32(x * scale))
+ */
+#ifndef FP8_LINEAR_H
+#define FP8_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FP8_E4M3 = 0, FP8_E5M2 = 1 } fp8_format;
+
+/* Per-tensor scaling of one quantized tensor. */
+typedef enum {
+    FP8_SCALE_TENSOR = 0,        /* one current amax for the whole tensor */
+    FP8_SCALE_BLOCK_1x128 = 1,   /* row layout: blocks of 1 row x 128 columns;
+                                    col layout: blocks of 128 rows x 1 column */
+    FP8_SCALE_BLOCK_128x128 = 2  /* 128x128 tiles, shared by both layouts */
+} fp8_scaling;
+
+/* Recipe of a whole linear layer. */
+typedef enum {
+    FP8_RECIPE_TENSOR = 0,       /* X, W, dY tensorwise */
+    FP8_RECIPE_BLOCK = 1         /* X, dY 1x128; W 128x128 */
+} fp8_recipe;
+
+enum { FP8_LAYOUT_ROW = 1, FP8_LAYOUT_COL = 2 };   /* bitmask */
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_NULL = 1,            /* a required pointer is NULL */
+    FP8_ERR_SHAPE = 2,           /* a dimension is not a positive multiple of 128 */
+    FP8_ERR_ALIGN = 3,           /* a pointer is not 16-byte aligned */
+    FP8_ERR_ENUM = 4,            /* unknown format / scaling / recipe / layout / flag */
+    FP8_ERR_WORKSPACE = 5,       /* ws_bytes smaller than the query returned */
+    FP8_ERR_CACHE_EMPTY = 6,     /* is_first_microbatch = 0 on a cache never filled */
+    FP8_ERR_CACHE_MISMATCH = 7,  /* cache shape or recipe differs from the call */
+    FP8_ERR_HIP = 8,             /* a kernel launch failed */
+    FP8_ERR_UNIMPLEMENTED = 9
+} fp8_status;
+
+/*
+ * A quantized tensor: caller-owned device buffers.  For a source of shape
+ * [R, C]:
+ *   q_row      [R, C] codes (row layout), or NULL when not requested
+ *   q_col      [C, R] codes (transposed layout), or NULL when not requested
+ *   scale, scale_inv
+ *              TENSOR:  1 float each
+ *              1x128:   [R, C/128] (scales of the row layout)
+ *              128x128: [R/128, C/128] (shared by both layouts)
+ *   scale_col, scale_inv_col
+ *              1x128 only: [C, R/128], scales of the col layout, block
+ *              (c, rb) covering x[rb*128 .. rb*128+127][c]; ignored otherwise
+ *   amax       optional (may be NULL): TENSOR: 1 float, the tensor's amax;
+ *              ignored for block scaling
+ */
+typedef struct {
+    void* q_row;
+    void* q_col;
+    float* scale;
+    float* scale_inv;
+    float* scale_col;
+    float* scale_inv_col;
+    float* amax;
+} fp8_qtensor;
+
+/* Opaque host-side weight-cache handle (holds shape, recipe, a valid bit and
+ * a fill counter; the quantized bytes live in caller buffers). */
+typedef struct fp8_wcache_s* fp8_wcache;
+
+/* ------------------------------------------------------------------ */
+
+/* Workspace bytes needed by fp8_quantize for a [rows, cols] source. */
+size_t fp8_quantize_workspace_bytes(int64_t rows, int64_t cols, fp8_scaling scaling);
+
+/*
+ * Quantize a bf16 tensor x [rows, cols] to FP8 with current scaling
+ * (amax computed now, from these values).  layouts is a bitmask of
+ * FP8_LAYOUT_ROW / FP8_LAYOUT_COL; both layouts come from one pass over x
+ * ("fused cast emits ordinary and transposed layouts", "Native FP8 MLP
+ * reconstruction", implementation paragraph).  Requesting a single layout
+ * gives bytes identical to those of the fused call.
+ * Writes out->q_row / out->q_col (as requested), out->scale, out->scale_inv,
+ * and for 1x128 with the col layout out->scale_col / out->scale_inv_col;
+ * out->amax if non-NULL and TENSOR.
+ */
+fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols,
+                        fp8_format format, fp8_scaling scaling, unsigned layouts,
+                        const fp8_qtensor* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Scale of an FP8 GEMM operand (dequantisation factors):
+ *   group == 0:  tensorwise, the factor is scale_inv[0]
+ *   group >= 1:  the factor of operand row r in contraction block kb
+ *                (128 contraction elements) is
+ *                scale_inv[(r / group) * stride_r + kb * stride_kb];
+ *                group is 1 (1x128 blocks) or 128 (128x128 blocks).
+ * Both operands of one GEMM must be tensorwise or both block-scaled.
+ */
+typedef struct {
+    const float* scale_inv;
+    int64_t group;
+    int64_t stride_r;
+    int64_t stride_kb;
+} fp8_gemm_scale;
+
+size_t fp8_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K);
+
+/*
+ * C[i][j] = bf16( sum_k A[i][k] * B[j][k] * scales ), A [I, K] and B [J, K]
+ * FP8 codes (both contraction-contiguous), C [I, J] bf16 row-major.
+ * fp32 accumulation on the FP8 matrix cores.  Tensorwise: the fp32 sum is
+ * multiplied by fl32(sA * sB) and rounded to bf16 (round to nearest even).
+ * Block-scaled: every 128-long contraction block's fp32 partial sum is
+ * multiplied by its two block factors and added to an fp32 accumulator.
+ * format_a may be E4M3 or E5M2; format_b likewise.
+ */
+fp8_status fp8_gemm(const void* a, fp8_format format_a, fp8_gemm_scale scale_a,
+                    const void* b, fp8_format format_b, fp8_gemm_scale scale_b,
+                    int64_t I, int64_t J, int64_t K, void* c_bf16,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------- weight cache --------------------------- */
+
+/*
+ * Create a cache for a weight [M, K] under `recipe`.  bufs names caller
+ * buffers for the quantized weight: q_row [M, K], q_col [K, M], scale and
+ * scale_inv (1 float for TENSOR; [M/128, K/128] for BLOCK).  The handle
+ * keeps these pointers; they must outlive it.  The cache starts empty.
+ */
+fp8_status fp8_wcache_create(int64_t M, int64_t K, fp8_recipe recipe,
+                             const fp8_qtensor* bufs, fp8_wcache* out);
+/* Mark the cache empty (e.g. after an optimizer step or loading weights). */
+fp8_status fp8_wcache_invalidate(fp8_wcache cache);
+/* 1 if the cache holds a quantized weight, 0 if empty, -1 on a NULL handle. */
+int fp8_wcache_valid(fp8_wcache cache);
+/* Number of times the cache has been filled since creation. */
+int64_t fp8_wcache_fills(fp8_wcache cache);
+void fp8_wcache_destroy(fp8_wcache cache);
+
+/* ---------------------------- linear layer --------------------------- */
+
+size_t fp8_linear_workspace_bytes(int64_t N, int64_t K, int64_t M, fp8_recipe recipe);
+
+/*
+ * Forward: Y [N, M] = X [N, K] W [M, K]^T in FP8 (E4M3 x E4M3), BF16 out.
+ *   saved_x  receives X quantized in both layouts (q_row [N, K], q_col [K, N])
+ *            with its scales; the backward pass reads its col layout.
+ *   Weight source, by is_first_microbatch:
+ *     -1 (None): W is quantized into w_q (both layouts); cache may be NULL
+ *                and is neither read nor written.
+ *      1 (True): W is quantized into the cache's buffers and the cache is
+ *                marked valid; w_q is ignored.
+ *      0 (False): the cache's quantized weight is used and w_bf16 is not
+ *                read (it may be NULL); FP8_ERR_CACHE_EMPTY if the cache was
+ *                never filled.
+ *   A cache whose M, K or recipe differ gives FP8_ERR_CACHE_MISMATCH.
+ */
+fp8_status fp8_linear_fwd(const void* x_bf16, const void* w_bf16,
+                          int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                          fp8_wcache cache, int is_first_microbatch,
+                          void* y_bf16, const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward: dY [N, M] is quantized to E5M2 (both layouts, its own current
+ * amax) into dy_q; then dX [N, K] = dY W (E5M2 x E4M3, W's col layout) and
+ * dW [M, K] = dY^T X (E5M2 x E4M3, both col layouts).  The weight comes from
+ * the cache when cache != NULL (it must be valid), else from w_q as written
+ * by fp8_linear_fwd.  dx_bf16 or dw_bf16 may be NULL to skip that GEMM.
+ */
+fp8_status fp8_linear_bwd(const void* dy_bf16, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                          const fp8_qtensor* saved_x, fp8_wcache cache, const fp8_qtensor* w_q,
+                          const fp8_qtensor* dy_q, void* dx_bf16, void* dw_bf16,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------- misc -------------------------------- */
+
+const char* fp8_status_string(fp8_status status);
+/* Message of the calling thread's most recent failure ("" if none). */
+const char* fp8_last_error(void);
+/* Library version string. */
+const char* fp8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8_LINEAR_H */

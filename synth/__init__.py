@@ -68,3 +68,15 @@ def bits(t):
 
 def sha256(t):
     return hashlib.sha256(bits(t).tobytes()).hexdigest()
+
+
+def operands_on_device(N, K, M, seed=0, sigma_x=1.0, sigma_w=0.02, sigma_dy=1e-3, device="cuda"):
+    """Same distributions as ``operands`` drawn with a seeded device generator
+    (for large timing runs where CPU drawing would dominate); drawn in the
+    order X, W, dY."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = (torch.randn((N, K), generator=g, device=device, dtype=torch.float32) * sigma_x).to(torch.bfloat16)
+    w = (torch.randn((M, K), generator=g, device=device, dtype=torch.float32) * sigma_w).to(torch.bfloat16)
+    dy = (torch.randn((N, M), generator=g, device=device, dtype=torch.float32) * sigma_dy).to(torch.bfloat16)
+    return x, w, dy

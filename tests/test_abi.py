@@ -1,0 +1,154 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/fp8_linear.h declares, and rejects bad arguments with
+the documented status before touching any device memory.  The pointers below
+are fake addresses: every call here must fail validation (no call may pass it
+and reach a kernel launch), so none is ever dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_mixed_precision_amax_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8_linear.h")
+
+OK, NULL, SHAPE, ALIGN, ENUM, WORKSPACE, CACHE_EMPTY, CACHE_MISMATCH = range(8)
+A = 0x7F0000000000          # a fake, 16-byte aligned "device" address
+U = A + 4                   # 4-byte aligned, not 16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(fp8_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert len(names) >= 15
+    assert sorted(names) == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.fp8_version().startswith(b"fp8linear")
+    for code, name in _lib.STATUS.items():
+        assert L.fp8_status_string(code).decode() == name
+
+
+def qt(**kw):
+    base = dict(q_row=A, q_col=A + 4096, scale=A + 8192, scale_inv=A + 8208, scale_col=A + 8224,
+                scale_inv_col=A + 8240, amax=None)
+    base.update(kw)
+    return _lib.QTensorC(**base)
+
+
+def quant(L, x=A, R=256, C=256, fmt=0, sc=0, lay=3, out=None, ws=A, wsb=4096):
+    out = qt() if out is None else out
+    return L.fp8_quantize(x, R, C, fmt, sc, lay, ctypes.byref(out), ws, wsb, None)
+
+
+def test_quantize_argument_errors(L):
+    assert quant(L, x=None) == NULL
+    assert quant(L, x=U) == ALIGN
+    assert quant(L, R=200) == SHAPE
+    assert quant(L, C=0) == SHAPE
+    assert quant(L, R=-128) == SHAPE
+    assert quant(L, fmt=2) == ENUM
+    assert quant(L, sc=3) == ENUM
+    assert quant(L, lay=0) == ENUM
+    assert quant(L, lay=4) == ENUM
+    assert quant(L, out=qt(q_row=None)) == NULL
+    assert quant(L, out=qt(q_col=A + 8)) == ALIGN
+    assert quant(L, out=qt(q_row=None), lay=1) == NULL
+    assert quant(L, out=qt(scale=None)) == NULL
+    assert quant(L, sc=1, out=qt(scale_col=None)) == NULL
+    assert quant(L, wsb=100) == WORKSPACE
+    assert quant(L, ws=None) == NULL
+    assert L.fp8_quantize(A, 256, 256, 0, 0, 3, None, A, 4096, None) == NULL
+
+
+def test_last_error_message(L):
+    assert quant(L, R=200) == SHAPE
+    assert b"multiple" in L.fp8_last_error()
+    assert quant(L, fmt=7) == ENUM
+    assert b"format" in L.fp8_last_error()
+
+
+def test_workspace_queries(L):
+    assert L.fp8_quantize_workspace_bytes(1024, 512, 0) >= 4096
+    assert L.fp8_quantize_workspace_bytes(1024, 512, 1) == 0
+    # a weight gradient with a long contraction uses split-K partials
+    assert L.fp8_gemm_workspace_bytes(2048, 512, 131072) > 0
+    assert L.fp8_linear_workspace_bytes(131072, 512, 2048, 0) >= L.fp8_gemm_workspace_bytes(2048, 512, 131072)
+
+
+def gs(p=A + 8192, group=0, sr=0, sk=0):
+    return _lib.GemmScaleC(p, group, sr, sk)
+
+
+def test_gemm_argument_errors(L):
+    def g(a=A, b=A, c=A, I=256, J=256, K=256, fa=0, fb=0, sa=None, sb=None, ws=A, wsb=1 << 30):
+        return L.fp8_gemm(a, fa, sa or gs(), b, fb, sb or gs(), I, J, K, c, ws, wsb, None)
+    assert g(a=None) == NULL
+    assert g(c=U) == ALIGN
+    assert g(K=100) == SHAPE
+    assert g(fa=5) == ENUM
+    assert g(sa=gs(group=1, sr=2, sk=1)) == ENUM          # mixed tensor / block
+    assert g(sa=gs(group=3), sb=gs(group=1)) == ENUM
+    assert g(sa=gs(p=None)) == NULL
+    assert g(I=256, J=256, K=131072, wsb=0) == WORKSPACE
+
+
+def make_cache(L, M=256, K=256, recipe=0, bufs=None):
+    h = ctypes.c_void_p()
+    st = L.fp8_wcache_create(M, K, recipe, ctypes.byref(bufs or qt()), ctypes.byref(h))
+    return st, h
+
+
+def test_cache_lifecycle_and_errors(L):
+    st, h = make_cache(L)
+    assert st == OK and h.value
+    assert L.fp8_wcache_valid(h) == 0 and L.fp8_wcache_fills(h) == 0
+    assert L.fp8_wcache_invalidate(h) == OK
+    assert L.fp8_wcache_valid(None) == -1
+    assert L.fp8_wcache_invalidate(None) == NULL
+    assert make_cache(L, M=100)[0] == SHAPE
+    assert make_cache(L, recipe=9)[0] == ENUM
+    assert make_cache(L, bufs=qt(q_col=None))[0] == NULL
+    assert L.fp8_wcache_create(256, 256, 0, ctypes.byref(qt()), None) == NULL
+    N, K, M = 256, 256, 256
+    wsb = L.fp8_linear_workspace_bytes(N, K, M, 0)
+    sx = qt()
+    # False on an empty cache
+    r = L.fp8_linear_fwd(A, None, N, K, M, 0, h, 0, A, ctypes.byref(sx), None, A, wsb, None)
+    assert r == CACHE_EMPTY
+    # shape / recipe mismatch
+    r = L.fp8_linear_fwd(A, A, N, K, 512, 0, h, 1, A, ctypes.byref(sx), None, A,
+                         L.fp8_linear_workspace_bytes(N, K, 512, 0), None)
+    assert r == CACHE_MISMATCH
+    r = L.fp8_linear_fwd(A, A, N, K, M, 1, h, 1, A, ctypes.byref(sx), None, A,
+                         L.fp8_linear_workspace_bytes(N, K, M, 1), None)
+    assert r == CACHE_MISMATCH
+    # bad flag, small workspace, None without w_q
+    assert L.fp8_linear_fwd(A, A, N, K, M, 0, h, 2, A, ctypes.byref(sx), None, A, wsb, None) == ENUM
+    assert L.fp8_linear_fwd(A, A, N, K, M, 0, h, 1, A, ctypes.byref(sx), None, A, 16, None) == WORKSPACE
+    assert L.fp8_linear_fwd(A, A, N, K, M, 0, None, -1, A, ctypes.byref(sx), None, A, wsb, None) == NULL
+    # backward through an empty cache
+    dq = qt()
+    r = L.fp8_linear_bwd(A, N, K, M, 0, ctypes.byref(sx), h, None, ctypes.byref(dq), A, A, A, wsb, None)
+    assert r == CACHE_EMPTY
+    assert L.fp8_linear_bwd(A, N, K, M, 0, ctypes.byref(sx), h, None, ctypes.byref(dq), None, None, A,
+                            wsb, None) == NULL
+    assert L.fp8_wcache_valid(h) == 0          # nothing above filled it
+    L.fp8_wcache_destroy(h)
+    L.fp8_wcache_destroy(None)
