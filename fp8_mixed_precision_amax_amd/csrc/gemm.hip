@@ -10,25 +10,32 @@
 //
 // Design (one kernel for all three GEMMs: every operand is contraction-
 // contiguous, "NT"):
-//  - workgroup 256 threads = 4 waves in 2x2; tile BM=256 (i) x BN (j) x BK=128;
-//    tensorwise BN=256 (wave 128x128 = 4x4 MFMA 32x32x64 blocks),
-//    block-scaled BN=128 (wave 128x64) so the per-block fp32 accumulators fit.
-//  - v_mfma_f32_32x32x64_f8f6f4 with the B tile as the matrix-core "A"
-//    operand, so each lane's accumulators hold one output row i and runs of
-//    4 consecutive columns j (8-byte bf16 runs in the epilogue).
-//  - global -> registers (16-byte loads) -> LDS, double-buffered, one barrier
-//    per K step; LDS rows are 128 bytes with the 16-byte chunk index XORed
-//    by (row/2)%8, so both the 16-byte stores and the fragment reads of 16
+//  - persistent: one workgroup per CU walks a list of work items (output tile,
+//    split-K slice); the software pipeline runs continuously across item
+//    boundaries, so the next tile's first K stages stream in while the
+//    current tile's epilogue stores go out.
+//  - workgroup 256 threads = 4 waves in 2x2; tensorwise tile 256x256, BK=64,
+//    4 LDS stages (wave 128x128 = 4x4 v_mfma_f32_32x32x64_f8f6f4 blocks);
+//    block-scaled tile 256x128, BK=128 (one scale block per K step), 3 stages
+//    (wave 128x64; per-block fp32 promotion needs the accumulators in VGPRs).
+//  - operands move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging):
+//    each instruction fills 1 KiB of LDS at M0 + 16 * lane; the lane picks
+//    its global 16-byte chunk so that the LDS rows come out XOR-swizzled
+//    (16-byte chunk index ^ f(row)), which makes the fragment reads of 16
 //    consecutive rows hit 16 distinct bank groups.
-//  - workgroup ids are remapped so consecutive tiles land on one XCD (the
-//    dispatcher deals workgroups round-robin over the 8 XCDs) and rastered in
-//    groups of 8 tile-rows for L2 reuse of A.
-//  - epilogue: scale, bf16 (v_cvt_pk_bf16_f32, round to nearest even), stage
-//    the tile in LDS (XOR-swizzled), write 16-byte coalesced rows.
-//  - split-K (for small outputs with long contractions, e.g. the weight
-//    gradient): each split writes fp32 partials; a reduce kernel sums the
-//    splits in fixed order (deterministic), applies the tensorwise factor
-//    and rounds to bf16.
+//  - stage hand-off: each wave waits with s_waitcnt vmcnt(n) for its own
+//    loads of the stage, then a plain s_barrier (no fence: a workgroup
+//    release fence would force vmcnt(0) and drain the prefetch queue).
+//  - the B tile is the matrix cores' "A" operand, so each lane's accumulators
+//    hold one output row i and runs of 4 consecutive columns j (8-byte bf16
+//    stores straight from registers).
+//  - work items are dealt so that the workgroups on one XCD (the dispatcher
+//    deals workgroups round-robin over the 8 XCDs) take consecutive items,
+//    rastered in groups of 8 tile-rows for L2 reuse of A.
+//  - split-K (small outputs with long contractions, e.g. the weight
+//    gradient): each slice writes fp32 partials; a reduce kernel sums the
+//    slices in fixed order (deterministic), applies the tensorwise factor and
+//    rounds to bf16.
 #include "internal.hpp"
 
 namespace fp8k {
@@ -37,9 +44,11 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 256;
-constexpr int kBK = 128;
 constexpr int kThreads = 256;
+
+template <bool BLOCK> struct Cfg;
+template <> struct Cfg<false> { static constexpr int BM = 256, BN = 256, BK = 64, S = 4, WNJ = 4; };
+template <> struct Cfg<true> { static constexpr int BM = 256, BN = 128, BK = 128, S = 3, WNJ = 2; };
 
 struct GemmArgs {
     const uint8_t* a;
@@ -50,7 +59,8 @@ struct GemmArgs {
     float* part;      // split-K partials [splits][I][J]
     int splits;
     int tiles_i, tiles_j;
-    int ktiles;       // K / 128
+    int ktiles;       // K / BK
+    int items;        // tiles_i * tiles_j * splits
 };
 
 template <int FA, int FB>
@@ -59,83 +69,166 @@ __device__ __forceinline__ v16f mfma(const v8i& bfrag, const v8i& afrag, const v
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfrag, afrag, c, FB, FA, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int kk, int lane) {
-    // 32 bytes of row `row`, logical 16-byte chunks kk*4 + (lane/32)*2 + {0,1}
-    const int swz = (row >> 1) & 7;
-    const int c0 = kk * 4 + (lane >> 5) * 2;
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * kBK + ((c0 ^ swz) << 4));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + row * kBK + (((c0 + 1) ^ swz) << 4));
+// XOR swizzle of the 16-byte chunk index of an LDS row
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+    return BK == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
+}
+
+// 32 bytes of LDS row `row` (logical 16-byte chunks c0, c0 + 1)
+template <int BK>
+__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int c0) {
+    const int s = swz<BK>(row);
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * BK + ((c0 ^ s) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + row * BK + (((c0 + 1) ^ s) << 4));
     return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Map the linear workgroup id to a (tile_i, tile_j) pair.
-__device__ __forceinline__ void tile_of(int bid, int tiles_i, int tiles_j, int& ti, int& tj) {
-    const int nwg = tiles_i * tiles_j;
-    if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);   // XCD-contiguous
-    constexpr int G = 8;
-    const int per_group = G * tiles_j;
-    const int g = bid / per_group;
-    const int local = bid - g * per_group;
-    int rows = tiles_i - g * G;
-    rows = rows < G ? rows : G;
-    ti = g * G + local % rows;
-    tj = local / rows;
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) for n in 0..63 (gfx9 encoding: low 4 bits + bits 15:14;
+// expcnt and lgkmcnt fields left at "no wait")
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+struct Item {
+    int ti, tj, z, kb, ke;
+};
+
+// r-th item of this workgroup.  Round r covers logical items
+// [r*G, (r+1)*G); a workgroup on XCD x = b % 8 takes the x-th eighth of it.
+__device__ __forceinline__ bool item_of(const GemmArgs& g, int r, Item& it) {
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int L = r * G + ((G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b);
+    if (L >= g.items) return false;
+    const int tiles = g.tiles_i * g.tiles_j;
+    const int z = L / tiles;
+    const int t = L - z * tiles;
+    constexpr int GI = 8;
+    const int per_group = GI * g.tiles_j;
+    const int grp = t / per_group;
+    const int local = t - grp * per_group;
+    int rows = g.tiles_i - grp * GI;
+    rows = rows < GI ? rows : GI;
+    it.ti = grp * GI + local % rows;
+    it.tj = local / rows;
+    it.z = z;
+    it.kb = (int)(((int64_t)g.ktiles * z) / g.splits);
+    it.ke = (int)(((int64_t)g.ktiles * (z + 1)) / g.splits);
+    return true;
 }
 
 template <int FA, int FB, bool BLOCK>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
-    constexpr int WNJ = BLOCK ? 2 : 4;          // 32-col blocks per wave in j
-    constexpr int BN = 2 * WNJ * 32;
-    constexpr int A_BYTES = kBM * kBK;
-    constexpr int B_BYTES = BN * kBK;
-    constexpr int STAGE = A_BYTES + B_BYTES;
-    constexpr int APASS = kBM / 32;             // 16-byte loads per thread for A
-    constexpr int BPASS = BN / 32;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
+    using C = Cfg<BLOCK>;
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::S, WNJ = C::WNJ;
+    constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+    // block mode: the stage also carries the fp32 factors of its 128-block,
+    // A rows [BM] then B rows [BN], loaded by 4-byte LDS-DMA
+    constexpr int SC_BYTES = BLOCK ? (BM + BN) * 4 : 0;
+    constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
+    constexpr int LA = A_BYTES / 1024 / 4, LB = B_BYTES / 1024 / 4;
+    constexpr int L = LA + LB + (BLOCK ? 2 : 0);   // LDS-DMA instructions per wave per stage
+    constexpr int RPK = 1024 / BK;   // rows per 1 KiB LDS block
+    constexpr int CPR = BK / 16;     // 16-byte chunks per row
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wi = wave >> 1, wj = wave & 1;
 
-    int ti, tj;
-    tile_of(blockIdx.x, g.tiles_i, g.tiles_j, ti, tj);
-    const int64_t i0 = (int64_t)ti * kBM;
-    const int64_t j0 = (int64_t)tj * BN;
-    const int z = blockIdx.y;
-    const int kt_begin = (int)(((int64_t)g.ktiles * z) / g.splits);
-    const int kt_end = (int)(((int64_t)g.ktiles * (z + 1)) / g.splits);
-
-    // ---- global load mapping: thread -> row tid/8 (+32p), 16-byte chunk tid%8
-    const int lrow = tid >> 3, lchunk = tid & 7;
-    const int sw_st = (lchunk ^ ((lrow >> 1) & 7)) << 4;
-    const bool a_hi_ok = (i0 + 128) < g.I;     // I is a multiple of 128
-    const bool b_hi_ok = (BN <= 128) || (j0 + 128) < g.J;
-    const uint8_t* gA = g.a + (i0 + lrow) * g.K + lchunk * 16;
-    const uint8_t* gB = g.b + (j0 + lrow) * g.K + lchunk * 16;
-
-    u32x4 ra[APASS], rb[BPASS];
-#define FP8K_LOAD_TILE(kt)                                                                  \
-    do {                                                                                    \
-        const int64_t koff_ = (int64_t)(kt) * kBK;                                          \
-        _Pragma("unroll") for (int p = 0; p < APASS; p++) {                                 \
-            const int pr = (p >= 4 && !a_hi_ok) ? p - 4 : p;                                \
-            ra[p] = *reinterpret_cast<const u32x4*>(gA + (int64_t)pr * 32 * g.K + koff_);   \
-        }                                                                                   \
-        _Pragma("unroll") for (int p = 0; p < BPASS; p++) {                                 \
-            const int pr = (p >= 4 && !b_hi_ok) ? p - 4 : p;                                \
-            rb[p] = *reinterpret_cast<const u32x4*>(gB + (int64_t)pr * 32 * g.K + koff_);   \
-        }                                                                                   \
+    // ---- load cursor (runs S-1 stages ahead of the compute cursor) -------
+    int l_round = 0, l_kt = 0;
+    Item l_it;
+    bool l_ok = item_of(g, 0, l_it);
+    // Per-lane load addresses.  Instruction p of this wave fills LDS block
+    // (wave*LA + p); its rows are those of p = 0 plus p*RPK, and the swizzled
+    // chunk is the same for every p (BK = 64) or alternates with p's parity
+    // (BK = 128: chunk ^ 4), so one base pointer and one parity delta per
+    // operand describe all of them.
+    const uint8_t* pa0 = nullptr;   // A rows of p = 0
+    const uint8_t* pb0 = nullptr;
+    int64_t a_hi = 0, b_hi = 0;      // shift for the upper 128 rows of a half-full tile
+    int dchunk = 0;                  // byte delta of odd p (BK = 128)
+    const float* psa = nullptr;      // block mode: scale row pointers of this lane
+    const float* psb = nullptr;
+    {
+        const int row0 = lane / CPR;
+        const int c0 = (lane % CPR) ^ swz<BK>(row0);
+        if (BK == 128) dchunk = (((lane % CPR) ^ swz<BK>(row0 + RPK)) - c0) * 16;
+    }
+#define FP8K_SET_LOAD_PTRS()                                                              \
+    do {                                                                                  \
+        const int64_t i0_ = (int64_t)l_it.ti * BM, j0_ = (int64_t)l_it.tj * BN;           \
+        const int rowa_ = wave * LA * RPK + lane / CPR;                                   \
+        const int rowb_ = wave * LB * RPK + lane / CPR;                                   \
+        const int c_ = (lane % CPR) ^ swz<BK>(lane / CPR);                                \
+        pa0 = g.a + (i0_ + rowa_) * g.K + c_ * 16;                                        \
+        pb0 = g.b + (j0_ + rowb_) * g.K + c_ * 16;                                        \
+        /* half-full last tile: rows >= 128 of the tile re-read rows - 128 */             \
+        a_hi = (i0_ + 128 >= g.I) ? -128 * g.K : 0;                                       \
+        b_hi = (j0_ + 128 >= g.J) ? -128 * g.K : 0;                                       \
+        if constexpr (BLOCK) {                                                            \
+            /* this lane's scale rows: A row wave*64+lane, B row (wave&1)*64+lane */       \
+            int64_t ra_ = i0_ + wave * 64 + lane;                                         \
+            ra_ = ra_ < g.I ? ra_ : g.I - 1;                                              \
+            int64_t rb_ = j0_ + (wave & 1) * 64 + lane;                                   \
+            rb_ = rb_ < g.J ? rb_ : g.J - 1;                                              \
+            psa = g.sa.sinv + (ra_ / g.sa.group) * g.sa.stride_r;                         \
+            psb = g.sb.sinv + (rb_ / g.sb.group) * g.sb.stride_r;                         \
+        }                                                                                 \
     } while (0)
-#define FP8K_STORE_TILE(stage)                                                              \
-    do {                                                                                    \
-        uint8_t* sA_ = smem + (stage) * STAGE;                                              \
-        uint8_t* sB_ = sA_ + A_BYTES;                                                       \
-        _Pragma("unroll") for (int p = 0; p < APASS; p++)                                   \
-            *reinterpret_cast<u32x4*>(sA_ + (lrow + 32 * p) * kBK + sw_st) = ra[p];         \
-        _Pragma("unroll") for (int p = 0; p < BPASS; p++)                                   \
-            *reinterpret_cast<u32x4*>(sB_ + (lrow + 32 * p) * kBK + sw_st) = rb[p];         \
+    if (l_ok) {
+        l_kt = l_it.kb;
+        FP8K_SET_LOAD_PTRS();
+    }
+    int issued = 0;   // stages issued so far
+    // row offset (in rows) of instruction p inside this wave's part of the tile
+#define FP8K_ROWOFF(p, rows_per_wave, hi)                                                          \
+    ((int64_t)(p) * RPK * g.K + (((wave * (rows_per_wave) + (p) * RPK) >= 128) ? (hi) : 0) +          \
+     (((p) & 1) ? dchunk : 0))
+#define FP8K_ISSUE_STAGE()                                                                         \
+    do {                                                                                           \
+        uint8_t* st_ = smem + (issued % S) * STAGE;                                                \
+        const int64_t koff_ = (int64_t)l_kt * BK;                                                  \
+        _Pragma("unroll") for (int p = 0; p < LA; p++)                                             \
+            __builtin_amdgcn_global_load_lds(pa0 + koff_ + FP8K_ROWOFF(p, LA * RPK, a_hi),        \
+                                             st_ + (wave * LA + p) * 1024, 16, 0, 0);              \
+        _Pragma("unroll") for (int p = 0; p < LB; p++)                                             \
+            __builtin_amdgcn_global_load_lds(pb0 + koff_ + FP8K_ROWOFF(p, LB * RPK, b_hi),        \
+                                             st_ + A_BYTES + (wave * LB + p) * 1024, 16, 0, 0);    \
+        if constexpr (BLOCK) {                                                                     \
+            __builtin_amdgcn_global_load_lds(psa + (int64_t)l_kt * g.sa.stride_kb,                \
+                                             st_ + A_BYTES + B_BYTES + wave * 256, 4, 0, 0);       \
+            __builtin_amdgcn_global_load_lds(psb + (int64_t)l_kt * g.sb.stride_kb,                \
+                                             st_ + A_BYTES + B_BYTES + BM * 4 + (wave & 1) * 256, 4, 0, 0); \
+        }                                                                                          \
+        issued++;                                                                                  \
+        if (++l_kt >= l_it.ke) {                                                                   \
+            l_ok = item_of(g, ++l_round, l_it);                                                    \
+            if (l_ok) {                                                                            \
+                l_kt = l_it.kb;                                                                    \
+                FP8K_SET_LOAD_PTRS();                                                              \
+            }                                                                                      \
+        }                                                                                          \
     } while (0)
+    // prologue: S-1 stages in flight
+#pragma unroll
+    for (int s = 0; s < S - 1; s++)
+        if (l_ok) FP8K_ISSUE_STAGE();
+
+    // ---- compute cursor ----------------------------------------------------
+    int c_round = 0;
+    Item c_it;
+    if (!item_of(g, 0, c_it)) return;
+    int c_kt = c_it.kb;
+    int consumed = 0;
 
     v16f acc[4][WNJ];
 #pragma unroll
@@ -145,157 +238,171 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[mi][nj][v] = 0.0f;
 
-    const int arow = wi * 128 + (lane & 31);
-    const int brow = wj * (WNJ * 32) + (lane & 31);
-    // rows (i) and column runs (j) owned by this lane in the accumulators
-    const int64_t my_i = i0 + arow;               // + mi*32
-    const int64_t my_j = j0 + wj * (WNJ * 32) + 4 * (lane >> 5);   // + nj*32 + 8q + r
-
-    // block-scale pointers
+    const int frow = lane & 31;                    // fragment row within a 32-row block
+    const int arow = wi * 128 + frow;
+    const int brow = wj * (WNJ * 32) + frow;
     const bool sb_per_row = BLOCK && g.sb.group == 1;
+    float t_tensor = 1.0f;
+    if constexpr (!BLOCK) t_tensor = g.sa.sinv[0] * g.sb.sinv[0];
 
-    if (kt_begin < kt_end) {
-        FP8K_LOAD_TILE(kt_begin);
-        FP8K_STORE_TILE(0);
-    }
-    __syncthreads();
+#define FP8K_STEP(FIRST)                                                                   \
+    do {                                                                                   \
+ /* Epilogue stores are younger than every issued stage, so counting only */ \
+ /* the stages issued after this one also waits for those stores: never */ \
+ /* too few (vmcnt completes in order), at worst a little early. */ \
+        const int younger = issued - consumed - 1; /* stages issued after it */ \
+        static_assert(2 * L <= 63, "vmcnt field is 6 bits"); \
+        if (younger >= 2) { \
+            wait_vm<2 * L>(); \
+        } else if (younger == 1) { \
+            wait_vm<L>(); \
+        } else { \
+            wait_vm<0>(); \
+        } \
+        barrier_lds(); \
+        if (l_ok) FP8K_ISSUE_STAGE(); \
+ \
+        const uint8_t* sA = smem + (consumed % S) * STAGE; \
+        const uint8_t* sB = sA + A_BYTES; \
+        if constexpr (!BLOCK) { \
+            v8i af[4], bf[WNJ]; \
+_Pragma("unroll") \
+            for (int mi = 0; mi < 4; mi++) af[mi] = lds_frag<BK>(sA, arow + mi * 32, (lane >> 5) * 2); \
+_Pragma("unroll") \
+            for (int nj = 0; nj < WNJ; nj++) bf[nj] = lds_frag<BK>(sB, brow + nj * 32, (lane >> 5) * 2); \
+_Pragma("unroll") \
+            for (int mi = 0; mi < 4; mi++) \
+_Pragma("unroll") \
+                for (int nj = 0; nj < WNJ; nj++) acc[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], FIRST ? vzero : acc[mi][nj]); \
+        } else { \
+ /* fp32 factors of this 128-long contraction block (staged in LDS); */ \
+ /* rows past I or J hold the factor of row I-1 / J-1 */ \
+            const float* sAs = reinterpret_cast<const float*>(sA + A_BYTES + B_BYTES); \
+            const float* sBs = sAs + BM; \
+            float sa_v[4]; \
+_Pragma("unroll") \
+            for (int mi = 0; mi < 4; mi++) sa_v[mi] = sAs[arow + mi * 32]; \
+            float sb_v[WNJ][16]; \
+            float sb_u = 0.0f; \
+            if (sb_per_row) { \
+                const int jb = wj * (WNJ * 32) + 4 * (lane >> 5); \
+_Pragma("unroll") \
+                for (int nj = 0; nj < WNJ; nj++) \
+_Pragma("unroll") \
+                    for (int q = 0; q < 4; q++) { \
+                        const float4 f = *reinterpret_cast<const float4*>(sBs + jb + nj * 32 + 8 * q); \
+                        sb_v[nj][4 * q] = f.x; \
+                        sb_v[nj][4 * q + 1] = f.y; \
+                        sb_v[nj][4 * q + 2] = f.z; \
+                        sb_v[nj][4 * q + 3] = f.w; \
+                    } \
+            } else { \
+                sb_u = sBs[wj * (WNJ * 32)]; \
+            } \
+            v16f p[4][WNJ]; \
+            { \
+                v8i af[4], bf[WNJ]; \
+_Pragma("unroll") \
+                for (int mi = 0; mi < 4; mi++) af[mi] = lds_frag<BK>(sA, arow + mi * 32, (lane >> 5) * 2); \
+_Pragma("unroll") \
+                for (int nj = 0; nj < WNJ; nj++) bf[nj] = lds_frag<BK>(sB, brow + nj * 32, (lane >> 5) * 2); \
+                const v16f zero = {}; \
+_Pragma("unroll") \
+                for (int mi = 0; mi < 4; mi++) \
+_Pragma("unroll") \
+                    for (int nj = 0; nj < WNJ; nj++) p[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], zero); \
+            } \
+            { \
+                v8i af[4], bf[WNJ]; \
+_Pragma("unroll") \
+                for (int mi = 0; mi < 4; mi++) af[mi] = lds_frag<BK>(sA, arow + mi * 32, 4 + (lane >> 5) * 2); \
+_Pragma("unroll") \
+                for (int nj = 0; nj < WNJ; nj++) bf[nj] = lds_frag<BK>(sB, brow + nj * 32, 4 + (lane >> 5) * 2); \
+_Pragma("unroll") \
+                for (int mi = 0; mi < 4; mi++) \
+_Pragma("unroll") \
+                    for (int nj = 0; nj < WNJ; nj++) p[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], p[mi][nj]); \
+            } \
+_Pragma("unroll") \
+            for (int mi = 0; mi < 4; mi++) \
+_Pragma("unroll") \
+                for (int nj = 0; nj < WNJ; nj++) { \
+                    if (sb_per_row) { \
+_Pragma("unroll") \
+                        for (int v = 0; v < 16; v++) \
+                            acc[mi][nj][v] = FIRST ? p[mi][nj][v] * (sa_v[mi] * sb_v[nj][v]) : __builtin_fmaf(p[mi][nj][v], sa_v[mi] * sb_v[nj][v], acc[mi][nj][v]); \
+                    } else { \
+                        const float t = sa_v[mi] * sb_u; \
+_Pragma("unroll") \
+                        for (int v = 0; v < 16; v++) acc[mi][nj][v] = FIRST ? p[mi][nj][v] * t : __builtin_fmaf(p[mi][nj][v], t, acc[mi][nj][v]); \
+                    } \
+                } \
+        } \
+        consumed++;                                                                        \
+    } while (0)
 
-    for (int kt = kt_begin; kt < kt_end; kt++) {
-        const int cur = (kt - kt_begin) & 1;
-        const bool more = kt + 1 < kt_end;
-        float sa_v[4];
-        float sb_u = 0.0f;
-        float sb_v[WNJ][16];
-        if constexpr (BLOCK) {
+    const v16f vzero = {};
+    (void)vzero;
+    while (true) {
+        FP8K_STEP(true);
+        for (int kt = c_it.kb + 1; kt < c_it.ke; kt++) {
+            c_kt = kt;
+            FP8K_STEP(false);
+        }
+        // ---- epilogue of the finished item ---------------------------------
+        {
+            const int64_t i0 = (int64_t)c_it.ti * BM, j0 = (int64_t)c_it.tj * BN;
+            const int64_t my_i = i0 + arow;
+            const int64_t jw = j0 + wj * (WNJ * 32);                  // first column of this wave
+            const int64_t my_j = jw + 4 * (lane >> 5);
+            // validity is uniform per 32x32 block (I, J are multiples of 128)
+            const bool i_ok0 = i0 + wi * 128 < g.I;                   // mi blocks share it
+            const int nj_ok = jw >= g.J ? 0 : WNJ;                    // wave's columns all valid or none
+            if (g.splits > 1) {
+                float* out = g.part + (int64_t)c_it.z * g.I * g.J + my_i * g.J + my_j;
+                if (i_ok0 && nj_ok) {
 #pragma unroll
-            for (int mi = 0; mi < 4; mi++)
-            {
-                // rows past I (upper half of a last, half-full tile) read row I-1's scale
-                const int64_t ii = my_i + mi * 32 < g.I ? my_i + mi * 32 : g.I - 1;
-                sa_v[mi] = g.sa.sinv[(ii / g.sa.group) * g.sa.stride_r + (int64_t)kt * g.sa.stride_kb];
-            }
-            if (sb_per_row) {
+                    for (int mi = 0; mi < 4; mi++)
 #pragma unroll
-                for (int nj = 0; nj < WNJ; nj++)
+                        for (int nj = 0; nj < WNJ; nj++)
 #pragma unroll
-                    for (int v = 0; v < 16; v++)
-                    {
-                        int64_t jj = my_j + nj * 32 + 8 * (v >> 2) + (v & 3);
-                        jj = jj < g.J ? jj : g.J - 1;
-                        sb_v[nj][v] = g.sb.sinv[jj * g.sb.stride_r + (int64_t)kt * g.sb.stride_kb];
-                    }
+                            for (int q = 0; q < 4; q++)
+                                *reinterpret_cast<float4*>(out + (int64_t)mi * 32 * g.J + nj * 32 + 8 * q) =
+                                    make_float4(acc[mi][nj][4 * q], acc[mi][nj][4 * q + 1], acc[mi][nj][4 * q + 2],
+                                                acc[mi][nj][4 * q + 3]);
+                }
             } else {
-                sb_u = g.sb.sinv[((j0 + wj * (WNJ * 32)) / g.sb.group) * g.sb.stride_r + (int64_t)kt * g.sb.stride_kb];
-            }
-        }
-        if (more) FP8K_LOAD_TILE(kt + 1);
-
-        const uint8_t* sA = smem + cur * STAGE;
-        const uint8_t* sB = sA + A_BYTES;
-        if constexpr (!BLOCK) {
+                const float t = BLOCK ? 1.0f : t_tensor;
+                uint16_t* out = g.c + my_i * g.J + my_j;
+                if (i_ok0 && nj_ok) {
 #pragma unroll
-            for (int kk = 0; kk < 2; kk++) {
-                v8i af[4], bf[WNJ];
+                    for (int mi = 0; mi < 4; mi++)
 #pragma unroll
-                for (int mi = 0; mi < 4; mi++) af[mi] = lds_frag(sA, arow + mi * 32, kk, lane);
+                        for (int nj = 0; nj < WNJ; nj++)
 #pragma unroll
-                for (int nj = 0; nj < WNJ; nj++) bf[nj] = lds_frag(sB, brow + nj * 32, kk, lane);
-#pragma unroll
-                for (int mi = 0; mi < 4; mi++)
-#pragma unroll
-                    for (int nj = 0; nj < WNJ; nj++) acc[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], acc[mi][nj]);
-            }
-        } else {
-            v8i af[2][4], bf[2][WNJ];
-#pragma unroll
-            for (int kk = 0; kk < 2; kk++) {
-#pragma unroll
-                for (int mi = 0; mi < 4; mi++) af[kk][mi] = lds_frag(sA, arow + mi * 32, kk, lane);
-#pragma unroll
-                for (int nj = 0; nj < WNJ; nj++) bf[kk][nj] = lds_frag(sB, brow + nj * 32, kk, lane);
-            }
-            const v16f zero = {};
-#pragma unroll
-            for (int mi = 0; mi < 4; mi++)
-#pragma unroll
-                for (int nj = 0; nj < WNJ; nj++) {
-                    v16f p = mfma<FA, FB>(bf[0][nj], af[0][mi], zero);
-                    p = mfma<FA, FB>(bf[1][nj], af[1][mi], p);
-                    if (sb_per_row) {
-#pragma unroll
-                        for (int v = 0; v < 16; v++)
-                            acc[mi][nj][v] = __builtin_fmaf(p[v], sa_v[mi] * sb_v[nj][v], acc[mi][nj][v]);
-                    } else {
-                        const float t = sa_v[mi] * sb_u;
-#pragma unroll
-                        for (int v = 0; v < 16; v++) acc[mi][nj][v] = __builtin_fmaf(p[v], t, acc[mi][nj][v]);
-                    }
+                            for (int q = 0; q < 4; q++) {
+                                const __bf16 h0 = (__bf16)(acc[mi][nj][4 * q] * t);
+                                const __bf16 h1 = (__bf16)(acc[mi][nj][4 * q + 1] * t);
+                                const __bf16 h2 = (__bf16)(acc[mi][nj][4 * q + 2] * t);
+                                const __bf16 h3 = (__bf16)(acc[mi][nj][4 * q + 3] * t);
+                                uint2 w;
+                                w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                      ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                                w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                      ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                                *reinterpret_cast<uint2*>(out + (int64_t)mi * 32 * g.J + nj * 32 + 8 * q) = w;
+                            }
                 }
-        }
-        if (more) FP8K_STORE_TILE(cur ^ 1);
-        __syncthreads();
-    }
-
-    // ---- epilogue -------------------------------------------------------
-    if (g.splits > 1) {
-        float* out = g.part + (int64_t)z * g.I * g.J;
-#pragma unroll
-        for (int mi = 0; mi < 4; mi++) {
-            const int64_t i = my_i + mi * 32;
-            if (i >= g.I) continue;
-#pragma unroll
-            for (int nj = 0; nj < WNJ; nj++)
-#pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int64_t j = my_j + nj * 32 + 8 * q;
-                    if (j < g.J)
-                        *reinterpret_cast<float4*>(out + i * g.J + j) =
-                            make_float4(acc[mi][nj][4 * q], acc[mi][nj][4 * q + 1], acc[mi][nj][4 * q + 2], acc[mi][nj][4 * q + 3]);
-                }
-        }
-        return;
-    }
-
-    float t = 1.0f;
-    if constexpr (!BLOCK) t = g.sa.sinv[0] * g.sb.sinv[0];
-    // stage the bf16 tile in LDS: row stride BN*2 bytes, 16-byte chunk c of
-    // row r stored at chunk c ^ (r % CH)
-    constexpr int CH = BN / 8;
-    uint8_t* sC = smem;
-#pragma unroll
-    for (int mi = 0; mi < 4; mi++)
-#pragma unroll
-        for (int nj = 0; nj < WNJ; nj++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int r = arow + mi * 32;
-                const int col = wj * (WNJ * 32) + nj * 32 + 8 * q;       // chunk-aligned
-                const int chunk = col >> 3;
-                const int off = r * (BN * 2) + ((chunk ^ (r & (CH - 1))) << 4) + (lane >> 5) * 8;
-                const __bf16 h0 = (__bf16)(acc[mi][nj][4 * q] * t);
-                const __bf16 h1 = (__bf16)(acc[mi][nj][4 * q + 1] * t);
-                const __bf16 h2 = (__bf16)(acc[mi][nj][4 * q + 2] * t);
-                const __bf16 h3 = (__bf16)(acc[mi][nj][4 * q + 3] * t);
-                uint2 w;
-                w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                *reinterpret_cast<uint2*>(sC + off) = w;
             }
-    __syncthreads();
-    // write rows: CH chunks of 16 bytes per row
-    constexpr int ROWS_PER_PASS = kThreads / CH;
-#pragma unroll 4
-    for (int r = tid / CH; r < kBM; r += ROWS_PER_PASS) {
-        const int c = tid % CH;
-        if (i0 + r >= g.I) break;
-        if (j0 + c * 8 >= g.J) continue;
-        const uint4 w = *reinterpret_cast<const uint4*>(sC + r * (BN * 2) + ((c ^ (r & (CH - 1))) << 4));
-        *reinterpret_cast<uint4*>(g.c + (i0 + r) * g.J + j0 + c * 8) = w;
+        }
+        if (!item_of(g, ++c_round, c_it)) break;
+        c_kt = c_it.kb;
     }
+#undef FP8K_SET_LOAD_PTRS
+#undef FP8K_ISSUE_STAGE
+#undef FP8K_ROWOFF
+#undef FP8K_STEP
 }
-
-#undef FP8K_LOAD_TILE
-#undef FP8K_STORE_TILE
 
 // Sum split-K partials in split order, apply the tensorwise factor, bf16.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t n4,
@@ -317,20 +424,33 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
-static int block_n(bool block) { return block ? 128 : 256; }
+static int block_n(bool block) { return block ? Cfg<true>::BN : Cfg<false>::BN; }
+static int block_k(bool block) { return block ? Cfg<true>::BK : Cfg<false>::BK; }
+
+static int cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
 
 int gemm_splits(int64_t I, int64_t J, int64_t K, bool block) {
-    const int64_t tiles = ((I + kBM - 1) / kBM) * ((J + block_n(block) - 1) / block_n(block));
-    const int64_t ktiles = K / kBK;
-    // aim for >= 2 workgroups per CU (256 CUs), keep >= 8 K tiles per split
+    const int64_t tiles = ((I + 255) / 256) * ((J + block_n(block) - 1) / block_n(block));
+    const int64_t k128 = K / 128;
+    // aim for >= 256 work items (one per CU), keep >= 8 blocks of 128 per split
     int64_t s = 1;
-    while (tiles * s < 512 && ktiles / (s * 2) >= 8 && s < 64) s *= 2;
+    while (tiles * s < 256 && k128 / (s * 2) >= 8 && s < 64) s *= 2;
     return (int)s;
 }
 
 size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K) {
-    const int s = gemm_splits(I, J, K, false) > gemm_splits(I, J, K, true) ? gemm_splits(I, J, K, false)
-                                                                            : gemm_splits(I, J, K, true);
+    const int a = gemm_splits(I, J, K, false), b = gemm_splits(I, J, K, true);
+    const int s = a > b ? a : b;
     return s > 1 ? (size_t)s * (size_t)I * (size_t)J * sizeof(float) : 0;
 }
 
@@ -348,11 +468,13 @@ hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream) {
     g.c = static_cast<uint16_t*>(l.c);
     g.part = static_cast<float*>(l.ws);
     g.splits = gemm_splits(l.I, l.J, l.K, block);
-    g.tiles_i = (int)((l.I + kBM - 1) / kBM);
+    g.tiles_i = (int)((l.I + 255) / 256);
     g.tiles_j = (int)((l.J + bn - 1) / bn);
-    g.ktiles = (int)(l.K / kBK);
-    const dim3 grid((unsigned)(g.tiles_i * g.tiles_j), (unsigned)g.splits);
-#define FP8K_GEMM(FA, FB, BL) hipLaunchKernelGGL((gemm_kernel<FA, FB, BL>), grid, dim3(kThreads), 0, stream, g)
+    g.ktiles = (int)(l.K / block_k(block));
+    g.items = g.tiles_i * g.tiles_j * g.splits;
+    int grid = cu_count();
+    if (grid > g.items) grid = g.items;
+#define FP8K_GEMM(FA, FB, BL) hipLaunchKernelGGL((gemm_kernel<FA, FB, BL>), dim3(grid), dim3(kThreads), 0, stream, g)
     if (l.fa == 0 && l.fb == 0) { if (block) FP8K_GEMM(0, 0, true); else FP8K_GEMM(0, 0, false); }
     else if (l.fa == 1 && l.fb == 0) { if (block) FP8K_GEMM(1, 0, true); else FP8K_GEMM(1, 0, false); }
     else if (l.fa == 0 && l.fb == 1) { if (block) FP8K_GEMM(0, 1, true); else FP8K_GEMM(0, 1, false); }

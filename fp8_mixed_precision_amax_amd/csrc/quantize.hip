@@ -11,13 +11,17 @@
 //                         packed 16-bit max on bf16 magnitude bits, wave and
 //                         workgroup reduction, one partial max per workgroup.
 //   cast_kernel<FMT,MODE> one wave per 128x128 tile, no LDS: lane (rb, cb)
-//                         owns rows rb*32..+31, columns cb*8..+7 of the tile
-//                         (16-byte coalesced loads, 256 contiguous bytes per
-//                         row per instruction); codes from the hardware
+//                         owns columns cb*8..+7 of rows rb*16..+15 and
+//                         64+rb*16..+15 (16-byte loads, 256 contiguous bytes
+//                         per row per instruction); codes from the hardware
 //                         converters (v_cvt_pk_fp8/bf8_f32, clamped first);
 //                         the transposed layout comes from in-register 4x4
-//                         byte transposes (v_perm_b32) and is written with
-//                         16-byte stores.
+//                         byte transposes (v_perm_b32).  The two 16-row
+//                         groups make every transposed store instruction
+//                         write whole 64-byte spans (4 lanes x 16 bytes),
+//                         issued as ordinary write-back stores so the L2
+//                         merges them; the row layout goes out with
+//                         non-temporal 8-byte stores (16 lanes = 128 bytes).
 //     MODE 0 tensorwise: the scale is rebuilt in each wave from the amax
 //            partials of pass 1 (so the cast needs no separate launch).
 //     MODE 1 1x128 blocks: row blocks reduce over the 16 lanes of a DPP row;
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4*
     for (; i + (kAmaxUnroll - 1) * stride < n16; i += kAmaxUnroll * stride) {
         uint4 v[kAmaxUnroll];
 #pragma unroll
-        for (int u = 0; u < kAmaxUnroll; u++) v[u] = ld_nt16(x + i + u * stride);
+        for (int u = 0; u < kAmaxUnroll; u++) v[u] = x[i + u * stride];
 #pragma unroll
         for (int u = 0; u < kAmaxUnroll; u++)
             m = pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v[u].x), mag2(v[u].y)), pkmax_u16(mag2(v[u].z), mag2(v[u].w))));
@@ -85,14 +89,16 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     if (tile >= ntiles) return;
     const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
     const int rb = lane >> 4, cb = lane & 15;
-    const int64_t row0 = tr * 128 + rb * 32;   // first of this lane's 32 rows
+    // this lane's rows: i < 16 -> rowA + i, i >= 16 -> rowB + (i - 16)
+    const int64_t rowA = tr * 128 + rb * 16;
+    const int64_t rowB = rowA + 64;
+#define FP8K_ROW(i) ((i) < 16 ? rowA + (i) : rowB + ((i) - 16))
     const int64_t col0 = tc * 128 + cb * 8;    // first of this lane's 8 columns
 
     // ---- load 32 rows x 8 bf16 ------------------------------------------
     uint4 v[32];
-    const uint16_t* src = a.x + row0 * a.C + col0;
 #pragma unroll
-    for (int i = 0; i < 32; i++) v[i] = ld_nt16(src + i * a.C);
+    for (int i = 0; i < 32; i++) v[i] = ld_nt16(a.x + FP8K_ROW(i) * a.C + col0);
 
     // ---- scales ---------------------------------------------------------
     float s_tile = 1.0f;          // MODE 0 and 2
@@ -135,8 +141,7 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
         }
         if (a.q_row) {
 #pragma unroll
-            for (int i = 0; i < 32; i++)
-                st_nt8(a.q_row + (row0 + i) * a.C + col0, code[i]);
+            for (int i = 0; i < 32; i++) st_nt8(a.q_row + FP8K_ROW(i) * a.C + col0, code[i]);
         }
         if (a.q_col) {
             uint32_t t[8][8];   // t[column j][row group h]
@@ -149,9 +154,9 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
             }
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                uint8_t* dst = a.q_col + (col0 + j) * a.R + row0;
-                st_nt16(dst, make_uint4(t[j][0], t[j][1], t[j][2], t[j][3]));
-                st_nt16(dst + 16, make_uint4(t[j][4], t[j][5], t[j][6], t[j][7]));
+                uint8_t* dst = a.q_col + (col0 + j) * a.R;
+                *reinterpret_cast<uint4*>(dst + rowA) = make_uint4(t[j][0], t[j][1], t[j][2], t[j][3]);
+                *reinterpret_cast<uint4*>(dst + rowB) = make_uint4(t[j][4], t[j][5], t[j][6], t[j][7]);
             }
         }
     } else {
@@ -177,10 +182,10 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
                     scale_from_amax_bits<FMT>(m, s, si);
                     uint2 c = enc8<FMT>(v[i], s);
                     if (m > 0x7F80u) c = patch_nan8(v[i], c);
-                    st_nt8(a.q_row + (row0 + i) * a.C + col0, c);
-                    if ((i >> 1) == cb) {   // lane cb writes rows 2cb, 2cb+1
-                        a.scale[(row0 + i) * cblocks + tc] = s;
-                        a.scale_inv[(row0 + i) * cblocks + tc] = si;
+                    st_nt8(a.q_row + FP8K_ROW(i) * a.C + col0, c);
+                    if ((i >> 1) == cb) {   // lane cb writes the scales of its rows 2cb, 2cb+1
+                        a.scale[FP8K_ROW(i) * cblocks + tc] = s;
+                        a.scale_inv[FP8K_ROW(i) * cblocks + tc] = si;
                     }
                 }
             }
@@ -232,12 +237,13 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
             }
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                uint8_t* dst = a.q_col + (col0 + j) * a.R + row0;
-                st_nt16(dst, make_uint4(t[j][0], t[j][1], t[j][2], t[j][3]));
-                st_nt16(dst + 16, make_uint4(t[j][4], t[j][5], t[j][6], t[j][7]));
+                uint8_t* dst = a.q_col + (col0 + j) * a.R;
+                *reinterpret_cast<uint4*>(dst + rowA) = make_uint4(t[j][0], t[j][1], t[j][2], t[j][3]);
+                *reinterpret_cast<uint4*>(dst + rowB) = make_uint4(t[j][4], t[j][5], t[j][6], t[j][7]);
             }
         }
     }
+#undef FP8K_ROW
 }
 
 int amax_partial_count(int64_t numel) {
