@@ -14,10 +14,12 @@
 //    split-K slice); the software pipeline runs continuously across item
 //    boundaries, so the next tile's first K stages stream in while the
 //    current tile's epilogue stores go out.
-//  - workgroup 256 threads = 4 waves in 2x2; tensorwise tile 256x256, BK=64,
-//    4 LDS stages (wave 128x128 = 4x4 v_mfma_f32_32x32x64_f8f6f4 blocks);
-//    block-scaled tile 256x128, BK=128 (one scale block per K step), 3 stages
-//    (wave 128x64; per-block fp32 promotion needs the accumulators in VGPRs).
+//  - workgroup 256 threads = 4 waves in 2x2, output tile 256x128 (wave tile
+//    128x64 = 4x2 v_mfma_f32_32x32x64_f8f6f4 blocks).  Tensorwise: BK=64, 2 LDS
+//    stages, two workgroups per CU (their loops interleave on each SIMD);
+//    block-scaled: BK=128 (one scale block per K step), 3 stages, one
+//    workgroup per CU (per-block fp32 promotion keeps the accumulators and
+//    the block partial sums in VGPRs).
 //  - operands move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging):
 //    each instruction fills 1 KiB of LDS at M0 + 16 * lane; the lane picks
 //    its global 16-byte chunk so that the LDS rows come out XOR-swizzled
@@ -27,8 +29,11 @@
 //    loads of the stage, then a plain s_barrier (no fence: a workgroup
 //    release fence would force vmcnt(0) and drain the prefetch queue).
 //  - the B tile is the matrix cores' "A" operand, so each lane's accumulators
-//    hold one output row i and runs of 4 consecutive columns j (8-byte bf16
-//    stores straight from registers).
+//    hold one output row i and runs of 4 consecutive columns j.  Tensorwise
+//    epilogue: each wave converts 32 rows at a time to bf16 into its own LDS
+//    slice and stores them back as whole 128-byte row segments (16 bytes per
+//    lane); the 8-byte register-layout stores touch 32 rows per instruction
+//    and write at less than half the HBM rate.
 //  - work items are dealt so that the workgroups on one XCD (the dispatcher
 //    deals workgroups round-robin over the 8 XCDs) take consecutive items,
 //    rastered in groups of 8 tile-rows for L2 reuse of A.
@@ -36,6 +41,8 @@
 //    gradient): each slice writes fp32 partials; a reduce kernel sums the
 //    slices in fixed order (deterministic), applies the tensorwise factor and
 //    rounds to bf16.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace fp8k {
@@ -46,9 +53,18 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
-template <bool BLOCK> struct Cfg;
-template <> struct Cfg<false> { static constexpr int BM = 256, BN = 256, BK = 64, S = 4, WNJ = 4; };
-template <> struct Cfg<true> { static constexpr int BM = 256, BN = 128, BK = 128, S = 3, WNJ = 2; };
+// Tile configuration: BM x BN output tile, BK contraction step, S LDS stages,
+// WNJ 32-column blocks per wave (wave tile 128 x 32*WNJ), OCC workgroups per
+// CU, EPI = 1 stages the bf16 epilogue through a per-wave LDS slice (32 rows
+// at a time) so every store instruction writes whole row segments.
+template <int BM_, int BN_, int BK_, int S_, int WNJ_, int OCC_, int EPI_ = 0>
+struct GemmCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WNJ = WNJ_, OCC = OCC_, EPI = EPI_;
+    static_assert(BM == 256 && BN == 2 * WNJ * 32, "4 waves in 2 x 2, wave tile 128 x 32*WNJ");
+    static_assert(BK == 64 || BK == 128, "BK");
+};
+using CfgTensor = GemmCfg<256, 128, 64, 2, 2, 2, 1>;
+using CfgBlock = GemmCfg<256, 128, 128, 3, 2, 1>;
 
 struct GemmArgs {
     const uint8_t* a;
@@ -123,9 +139,8 @@ __device__ __forceinline__ bool item_of(const GemmArgs& g, int r, Item& it) {
     return true;
 }
 
-template <int FA, int FB, bool BLOCK>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
-    using C = Cfg<BLOCK>;
+template <int FA, int FB, bool BLOCK, class C>
+__global__ __launch_bounds__(kThreads, C::OCC) void gemm_kernel(GemmArgs g) {
     constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::S, WNJ = C::WNJ;
     constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
     // block mode: the stage also carries the fp32 factors of its 128-block,
@@ -136,7 +151,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
     constexpr int L = LA + LB + (BLOCK ? 2 : 0);   // LDS-DMA instructions per wave per stage
     constexpr int RPK = 1024 / BK;   // rows per 1 KiB LDS block
     constexpr int CPR = BK / 16;     // 16-byte chunks per row
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+    constexpr int ECH = WNJ * 4;     // 16-byte chunks per epilogue row (32*WNJ bf16)
+    constexpr int EPI_BYTES = C::EPI ? 4 * 32 * ECH * 16 : 0;   // four per-wave slices
+    static_assert(S * STAGE + EPI_BYTES <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + EPI_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -189,6 +207,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
         FP8K_SET_LOAD_PTRS();
     }
     int issued = 0;   // stages issued so far
+    // vmcnt bookkeeping (wave-uniform): ops = vector-memory instructions
+    // issued so far (LDS-DMA loads and epilogue stores); pendK = value of ops
+    // right after the K-th oldest not-yet-consumed stage was issued.
+    int ops = 0, npend = 0, pend0 = 0, pend1 = 0, pend2 = 0;
     // row offset (in rows) of instruction p inside this wave's part of the tile
 #define FP8K_ROWOFF(p, rows_per_wave, hi)                                                          \
     ((int64_t)(p) * RPK * g.K + (((wave * (rows_per_wave) + (p) * RPK) >= 128) ? (hi) : 0) +          \
@@ -210,6 +232,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
                                              st_ + A_BYTES + B_BYTES + BM * 4 + (wave & 1) * 256, 4, 0, 0); \
         }                                                                                          \
         issued++;                                                                                  \
+        ops += L;                                                                                  \
+        if (npend == 0) pend0 = ops;                                                               \
+        else if (npend == 1) pend1 = ops;                                                          \
+        else pend2 = ops;                                                                          \
+        npend++;                                                                                   \
         if (++l_kt >= l_it.ke) {                                                                   \
             l_ok = item_of(g, ++l_round, l_it);                                                    \
             if (l_ok) {                                                                            \
@@ -247,17 +274,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
 
 #define FP8K_STEP(FIRST)                                                                   \
     do {                                                                                   \
- /* Epilogue stores are younger than every issued stage, so counting only */ \
- /* the stages issued after this one also waits for those stores: never */ \
- /* too few (vmcnt completes in order), at worst a little early. */ \
-        const int younger = issued - consumed - 1; /* stages issued after it */ \
-        static_assert(2 * L <= 63, "vmcnt field is 6 bits"); \
-        if (younger >= 2) { \
-            wait_vm<2 * L>(); \
-        } else if (younger == 1) { \
-            wait_vm<L>(); \
-        } else { \
-            wait_vm<0>(); \
+ /* vmcnt completes in order: waiting until at most n ops are outstanding, \
+   n = ops issued after this stage (capped at 63, rounded down to a multiple \
+   of 4), guarantees the stage landed while later stages and epilogue stores \
+   stay in flight. */ \
+        { \
+            const int n_after = ops - pend0; \
+            pend0 = pend1; \
+            pend1 = pend2; \
+            npend--; \
+            if (n_after >= 63) wait_vm<63>(); \
+            else if (n_after >= 56) wait_vm<56>(); \
+            else if (n_after >= 48) wait_vm<48>(); \
+            else if (n_after >= 40) wait_vm<40>(); \
+            else if (n_after >= 32) wait_vm<32>(); \
+            else if (n_after >= 28) wait_vm<28>(); \
+            else if (n_after >= 24) wait_vm<24>(); \
+            else if (n_after >= 20) wait_vm<20>(); \
+            else if (n_after >= 16) wait_vm<16>(); \
+            else if (n_after >= 14) wait_vm<14>(); \
+            else if (n_after >= 12) wait_vm<12>(); \
+            else if (n_after >= 8) wait_vm<8>(); \
+            else if (n_after >= 4) wait_vm<4>(); \
+            else wait_vm<0>(); \
         } \
         barrier_lds(); \
         if (l_ok) FP8K_ISSUE_STAGE(); \
@@ -265,15 +304,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g) {
         const uint8_t* sA = smem + (consumed % S) * STAGE; \
         const uint8_t* sB = sA + A_BYTES; \
         if constexpr (!BLOCK) { \
-            v8i af[4], bf[WNJ]; \
+            /* BK/64 matrix-core steps; the fragments of step kk+1 are read \
+               from LDS before the MFMAs of step kk are issued */ \
+            constexpr int KK = BK / 64; \
+            v8i af[2][4], bf[2][WNJ]; \
 _Pragma("unroll") \
-            for (int mi = 0; mi < 4; mi++) af[mi] = lds_frag<BK>(sA, arow + mi * 32, (lane >> 5) * 2); \
+            for (int mi = 0; mi < 4; mi++) af[0][mi] = lds_frag<BK>(sA, arow + mi * 32, (lane >> 5) * 2); \
 _Pragma("unroll") \
-            for (int nj = 0; nj < WNJ; nj++) bf[nj] = lds_frag<BK>(sB, brow + nj * 32, (lane >> 5) * 2); \
+            for (int nj = 0; nj < WNJ; nj++) bf[0][nj] = lds_frag<BK>(sB, brow + nj * 32, (lane >> 5) * 2); \
 _Pragma("unroll") \
-            for (int mi = 0; mi < 4; mi++) \
+            for (int kk = 0; kk < KK; kk++) { \
+                if (kk + 1 < KK) { \
 _Pragma("unroll") \
-                for (int nj = 0; nj < WNJ; nj++) acc[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], FIRST ? vzero : acc[mi][nj]); \
+                    for (int mi = 0; mi < 4; mi++) \
+                        af[(kk + 1) & 1][mi] = lds_frag<BK>(sA, arow + mi * 32, 4 * (kk + 1) + (lane >> 5) * 2); \
+_Pragma("unroll") \
+                    for (int nj = 0; nj < WNJ; nj++) \
+                        bf[(kk + 1) & 1][nj] = lds_frag<BK>(sB, brow + nj * 32, 4 * (kk + 1) + (lane >> 5) * 2); \
+                } \
+_Pragma("unroll") \
+                for (int mi = 0; mi < 4; mi++) \
+_Pragma("unroll") \
+                    for (int nj = 0; nj < WNJ; nj++) \
+                        acc[mi][nj] = mfma<FA, FB>(bf[kk & 1][nj], af[kk & 1][mi], \
+                                                   (FIRST && kk == 0) ? vzero : acc[mi][nj]); \
+            } \
         } else { \
  /* fp32 factors of this 128-long contraction block (staged in LDS); */ \
  /* rows past I or J hold the factor of row I-1 / J-1 */ \
@@ -358,6 +413,8 @@ _Pragma("unroll") \
             // validity is uniform per 32x32 block (I, J are multiples of 128)
             const bool i_ok0 = i0 + wi * 128 < g.I;                   // mi blocks share it
             const int nj_ok = jw >= g.J ? 0 : WNJ;                    // wave's columns all valid or none
+            // the wave issues all of the stores below or none of them
+            if (i_ok0 && nj_ok) ops += (C::EPI && g.splits == 1) ? 4 * (32 * ECH / 64) : 4 * WNJ * 4;
             if (g.splits > 1) {
                 float* out = g.part + (int64_t)c_it.z * g.I * g.J + my_i * g.J + my_j;
                 if (i_ok0 && nj_ok) {
@@ -370,6 +427,41 @@ _Pragma("unroll") \
                                 *reinterpret_cast<float4*>(out + (int64_t)mi * 32 * g.J + nj * 32 + 8 * q) =
                                     make_float4(acc[mi][nj][4 * q], acc[mi][nj][4 * q + 1], acc[mi][nj][4 * q + 2],
                                                 acc[mi][nj][4 * q + 3]);
+                }
+            } else if constexpr (C::EPI) {
+                // per-wave slice: 32 rows x ECH chunks, chunk c of row r stored at c ^ (r % ECH)
+                const float t = BLOCK ? 1.0f : t_tensor;
+                uint8_t* slice = smem + S * STAGE + wave * (32 * ECH * 16);
+                // row-major read-back: lane covers chunk (idx % ECH) of row (idx / ECH)
+                uint16_t* out_base = g.c + (i0 + wi * 128) * g.J + jw;
+                if (i_ok0 && nj_ok) {
+#pragma unroll
+                    for (int mi = 0; mi < 4; mi++) {
+#pragma unroll
+                        for (int nj = 0; nj < WNJ; nj++)
+#pragma unroll
+                            for (int q = 0; q < 4; q++) {
+                                const __bf16 h0 = (__bf16)(acc[mi][nj][4 * q] * t);
+                                const __bf16 h1 = (__bf16)(acc[mi][nj][4 * q + 1] * t);
+                                const __bf16 h2 = (__bf16)(acc[mi][nj][4 * q + 2] * t);
+                                const __bf16 h3 = (__bf16)(acc[mi][nj][4 * q + 3] * t);
+                                uint2 w;
+                                w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                                      ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                                w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
+                                      ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                                const int chunk = nj * 4 + q;
+                                *reinterpret_cast<uint2*>(slice + frow * (ECH * 16) + ((chunk ^ (frow % ECH)) << 4) +
+                                                          (lane >> 5) * 8) = w;
+                            }
+#pragma unroll
+                        for (int p = 0; p < 32 * ECH / 64; p++) {
+                            const int idx = p * 64 + lane;
+                            const int r = idx / ECH, c = idx % ECH;
+                            const uint4 w = *reinterpret_cast<const uint4*>(slice + r * (ECH * 16) + ((c ^ (r % ECH)) << 4));
+                            *reinterpret_cast<uint4*>(out_base + (int64_t)(mi * 32 + r) * g.J + c * 8) = w;
+                        }
+                    }
                 }
             } else {
                 const float t = BLOCK ? 1.0f : t_tensor;
@@ -424,8 +516,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
-static int block_n(bool block) { return block ? Cfg<true>::BN : Cfg<false>::BN; }
-static int block_k(bool block) { return block ? Cfg<true>::BK : Cfg<false>::BK; }
+static int block_n(bool block) { return block ? CfgBlock::BN : CfgTensor::BN; }
+static int block_k(bool block) { return block ? CfgBlock::BK : CfgTensor::BK; }
+static int block_occ(bool block) { return block ? CfgBlock::OCC : CfgTensor::OCC; }
 
 static int cu_count() {
     static int cache[64] = {0};
@@ -442,9 +535,11 @@ static int cu_count() {
 int gemm_splits(int64_t I, int64_t J, int64_t K, bool block) {
     const int64_t tiles = ((I + 255) / 256) * ((J + block_n(block) - 1) / block_n(block));
     const int64_t k128 = K / 128;
-    // aim for >= 256 work items (one per CU), keep >= 8 blocks of 128 per split
+    // aim for one work item per resident workgroup (256 CUs x occupancy),
+    // keep >= 8 blocks of 128 per split
+    const int64_t slots = 256 * block_occ(block);
     int64_t s = 1;
-    while (tiles * s < 256 && k128 / (s * 2) >= 8 && s < 64) s *= 2;
+    while (tiles * s < slots && k128 / (s * 2) >= 8 && s < 64) s *= 2;
     return (int)s;
 }
 
@@ -472,9 +567,11 @@ hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream) {
     g.tiles_j = (int)((l.J + bn - 1) / bn);
     g.ktiles = (int)(l.K / block_k(block));
     g.items = g.tiles_i * g.tiles_j * g.splits;
-    int grid = cu_count();
+    int grid = cu_count() * block_occ(block);
     if (grid > g.items) grid = g.items;
-#define FP8K_GEMM(FA, FB, BL) hipLaunchKernelGGL((gemm_kernel<FA, FB, BL>), dim3(grid), dim3(kThreads), 0, stream, g)
+#define FP8K_GEMM(FA, FB, BL) \
+    hipLaunchKernelGGL((gemm_kernel<FA, FB, BL, typename std::conditional<BL, CfgBlock, CfgTensor>::type>), \
+                       dim3(grid), dim3(kThreads), 0, stream, g)
     if (l.fa == 0 && l.fb == 0) { if (block) FP8K_GEMM(0, 0, true); else FP8K_GEMM(0, 0, false); }
     else if (l.fa == 1 && l.fb == 0) { if (block) FP8K_GEMM(1, 0, true); else FP8K_GEMM(1, 0, false); }
     else if (l.fa == 0 && l.fb == 1) { if (block) FP8K_GEMM(0, 1, true); else FP8K_GEMM(0, 1, false); }
