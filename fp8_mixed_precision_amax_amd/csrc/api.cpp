@@ -48,7 +48,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool dim_ok(int64_t d) { return d > 0 && (d % 128) == 0 && d <= (int64_t(1) << 31); }
 
-constexpr size_t kPartialBytes = 4096;   // tensorwise amax partials (1024 words)
+constexpr size_t kPartialBytes = 4096;   // tensorwise amax partials (2048 x 16 bits)
 
 fp8_status check_dims(const char* what, int64_t a, int64_t b) {
     if (!dim_ok(a) || !dim_ok(b))
@@ -120,7 +120,7 @@ fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, in
     q.scale_col = out->scale_col;
     q.scale_inv_col = out->scale_inv_col;
     q.amax = scaling == FP8_SCALE_TENSOR ? out->amax : nullptr;
-    q.partial = static_cast<uint32_t*>(ws);
+    q.partial = static_cast<uint16_t*>(ws);
     return hip_status(fp8k::launch_quantize(q, st), "quantize launch");
 }
 

@@ -7,7 +7,7 @@
 
 namespace fp8k {
 
-constexpr int kMaxAmaxPartials = 1024;
+constexpr int kMaxAmaxPartials = 2048;   // 16-bit slots, a multiple of 512
 
 struct QuantizeLaunch {
     const void* x;      // [rows, cols] bf16
@@ -21,7 +21,7 @@ struct QuantizeLaunch {
     float* scale_col;
     float* scale_inv_col;
     float* amax;        // optional
-    uint32_t* partial;  // tensor: kMaxAmaxPartials words of scratch
+    uint16_t* partial;  // tensor: kMaxAmaxPartials 16-bit slots of scratch (16-byte aligned)
 };
 
 int amax_partial_count(int64_t numel);

@@ -35,23 +35,18 @@
 namespace fp8k {
 
 constexpr int kAmaxThreads = 256;
-constexpr int kAmaxUnroll = 4;
 
+// One sweep of the tensor from front to back (grid-stride, one 16-byte load
+// per thread per step), so the cast that follows can start on the most
+// recently read data while it is still in the memory-side cache.  Partial
+// maxima are bf16 magnitude bits (16 bits); workgroup 0 zero-fills the
+// unused tail of the kMaxAmaxPartials slots so readers may scan all of them.
 __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
-                                                                    uint32_t* __restrict__ partial) {
+                                                                    uint16_t* __restrict__ partial) {
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
-    for (; i + (kAmaxUnroll - 1) * stride < n16; i += kAmaxUnroll * stride) {
-        uint4 v[kAmaxUnroll];
-#pragma unroll
-        for (int u = 0; u < kAmaxUnroll; u++) v[u] = x[i + u * stride];
-#pragma unroll
-        for (int u = 0; u < kAmaxUnroll; u++)
-            m = pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v[u].x), mag2(v[u].y)), pkmax_u16(mag2(v[u].z), mag2(v[u].w))));
-    }
-    for (; i < n16; i += stride) {
-        uint4 v = x[i];
+    for (int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n16; i += stride) {
+        const uint4 v = x[i];
         m = pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v.x), mag2(v.y)), pkmax_u16(mag2(v.z), mag2(v.w))));
     }
     m = wave_max_u32(hmax_u16(m));
@@ -61,8 +56,10 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4*
     if (threadIdx.x == 0) {
         uint32_t r = red[0];
         for (int w = 1; w < kAmaxThreads / 64; w++) r = r > red[w] ? r : red[w];
-        partial[blockIdx.x] = r;
+        partial[blockIdx.x] = (uint16_t)r;
     }
+    if (blockIdx.x == 0)
+        for (int p = (int)gridDim.x + threadIdx.x; p < kMaxAmaxPartials; p += kAmaxThreads) partial[p] = 0;
 }
 
 struct CastArgs {
@@ -75,8 +72,7 @@ struct CastArgs {
     float* scale_col;   // 1x128 only: [C, R/128]
     float* scale_inv_col;
     float* amax_out;    // tensor only, optional
-    const uint32_t* partial;  // tensor only: amax partials of pass 1
-    int npartial;
+    const uint16_t* partial;  // tensor only: kMaxAmaxPartials amax partials of pass 1 (unused slots 0)
 };
 
 template <int FMT, int MODE>
@@ -85,8 +81,11 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     const int wave = threadIdx.x >> 6;
     const int64_t tiles_c = a.C >> 7;
     const int64_t ntiles = (a.R >> 7) * tiles_c;
-    const int64_t tile = (int64_t)blockIdx.x * 4 + wave;
-    if (tile >= ntiles) return;
+    // tensorwise: last tile first (the amax pass swept front to back, so the
+    // tail of the tensor is the part most likely still cached)
+    const int64_t slot = (int64_t)blockIdx.x * 4 + wave;
+    if (slot >= ntiles) return;
+    const int64_t tile = MODE == 0 ? ntiles - 1 - slot : slot;
     const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
     const int rb = lane >> 4, cb = lane & 15;
     // this lane's rows: i < 16 -> rowA + i, i >= 16 -> rowB + (i - 16)
@@ -94,6 +93,14 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     const int64_t rowB = rowA + 64;
 #define FP8K_ROW(i) ((i) < 16 ? rowA + (i) : rowB + ((i) - 16))
     const int64_t col0 = tc * 128 + cb * 8;    // first of this lane's 8 columns
+
+    // tensorwise: the amax partials (issued first, they return first)
+    uint4 pw[kMaxAmaxPartials / 512];
+    if constexpr (MODE == 0) {
+#pragma unroll
+        for (int r = 0; r < kMaxAmaxPartials / 512; r++)
+            pw[r] = reinterpret_cast<const uint4*>(a.partial)[r * 64 + lane];
+    }
 
     // ---- load 32 rows x 8 bf16 ------------------------------------------
     uint4 v[32];
@@ -105,12 +112,14 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     bool nan_any = false;
     if constexpr (MODE == 0) {
         uint32_t m = 0;
-        for (int p = lane; p < a.npartial; p += 64) m = m > a.partial[p] ? m : a.partial[p];
-        m = wave_max_u32(m);
+#pragma unroll
+        for (int r = 0; r < kMaxAmaxPartials / 512; r++)
+            m = pkmax_u16(m, pkmax_u16(pkmax_u16(pw[r].x, pw[r].y), pkmax_u16(pw[r].z, pw[r].w)));
+        m = wave_max_u32(hmax_u16(m));
         float si;
         scale_from_amax_bits<FMT>(m, s_tile, si);
         nan_any = m > 0x7F80u;
-        if (tile == 0 && lane == 0) {
+        if (slot == 0 && lane == 0) {
             a.scale[0] = s_tile;
             a.scale_inv[0] = si;
             if (a.amax_out) a.amax_out[0] = m > 0x7F80u ? __uint_as_float(0x7FC00000u) : __uint_as_float(m << 16);
@@ -247,8 +256,9 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
 }
 
 int amax_partial_count(int64_t numel) {
+    // about eight workgroups per CU, one 16-byte load per thread per sweep step
     const int64_t n16 = numel / 8;
-    int64_t g = (n16 + (int64_t)kAmaxThreads * kAmaxUnroll * 8 - 1) / ((int64_t)kAmaxThreads * kAmaxUnroll * 8);
+    int64_t g = (n16 + (int64_t)kAmaxThreads * 16 - 1) / ((int64_t)kAmaxThreads * 16);
     if (g < 1) g = 1;
     if (g > kMaxAmaxPartials) g = kMaxAmaxPartials;
     return (int)g;
@@ -267,10 +277,8 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     a.scale_inv_col = q.scale_inv_col;
     a.amax_out = q.amax;
     a.partial = q.partial;
-    a.npartial = 0;
     if (q.scaling == 0) {
         const int g = amax_partial_count(q.rows * q.cols);
-        a.npartial = g;
         hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(kAmaxThreads), 0, stream,
                            static_cast<const uint4*>(q.x), q.rows * q.cols / 8, q.partial);
         hipError_t e = hipGetLastError();
