@@ -11,11 +11,21 @@ dY ~ N(0,1e-3)) resident in HBM.
 
 Prints ONE JSON line: the metric (TFLOP/s = 6 N K M summed over the two
 linears / step time), the quantize GB/s, per-stage times, the roofline of the
-dominant kernel and the oracle's throughput on host cores (cpu_baseline).
+dominant stage and the oracle's throughput on host cores (cpu_baseline).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+Profile summaries (no GPU needed): walks a rocprofv3 kernel trace or counter
+collection of a bench run, assigns each library dispatch of the timed steps to
+its stage (the step's call order is fixed), and prints markdown tables.
+
+    python bench.py --summarize DIR/PREFIX --steps K --warmup W
 """
 import argparse
+import collections
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -39,9 +49,182 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=int, default=131072)
     ap.add_argument("--reps", type=int, default=20, help="repetitions per stage in the breakdown")
-    ap.add_argument("--cpu-tokens", type=int, default=65536, help="token sample of the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-stage breakdown")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="after the steps, negate a 512 MiB fp16 tensor (counter calibration)")
+    ap.add_argument("--summarize", metavar="PREFIX", help="summarize PREFIX_kernel_trace.csv / "
+                    "PREFIX_counter_collection.csv of a profiled bench run and exit")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_PREFIX", "WRITE_PREFIX"),
+                    help="per-stage HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE counter run "
+                         "(each with --copy-reference), one line per stage, and exit")
     return ap.parse_args()
+
+
+SHAPES = [(512, 2048), (2048, 512)]
+KINDS = (("amax_partial_kernel", "amax"), ("cast_kernel", "cast"), ("gemm_kernel", "gemm"),
+         ("splitk_reduce_kernel", "reduce"))
+COPY_BYTES = 2 * 512 * 1024 * 1024      # the --copy-reference kernel reads 512 MiB and writes 512 MiB
+
+
+def step_sequence(shapes):
+    """Library calls of one step, in launch order, with the kernels each
+    launches (tensorwise recipe, weight requantized every step)."""
+    seq = []
+    for K, M in shapes:
+        tag = "%dx%d" % (K, M)
+        seq += [("quant_w_" + tag, ("amax", "cast")), ("quant_x_" + tag, ("amax", "cast")),
+                ("gemm_fprop_" + tag, ("gemm",)), ("quant_dy_" + tag, ("amax", "cast")),
+                ("gemm_dgrad_" + tag, ("gemm",)), ("gemm_wgrad_" + tag, ("gemm",))]
+    return seq
+
+
+def kernel_kind(name):
+    for key, kind in KINDS:
+        if "fp8k::" + key in name:
+            return kind
+    return None
+
+
+def short_name(name):
+    return name.replace("void ", "").replace("fp8k::", "")
+
+
+def source_digest():
+    """sha256 over the HIP/C++ sources and headers of the library."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "fp8_mixed_precision_amax_amd", "csrc", "*")) +
+                   glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def walk_steps(disp, steps, warmup):
+    """disp: [(kind, name, value)] of library dispatches in dispatch order.
+    Returns the timed steps as lists of (stage, kind, name, value)."""
+    seq = step_sequence(SHAPES)
+    i, out = 0, []
+    for s in range(warmup + steps):
+        cur = []
+        for stage, kinds in seq:
+            for kd in kinds:
+                if i >= len(disp) or disp[i][0] != kd:
+                    raise SystemExit("dispatch %d: expected a %s kernel for %s, found %s" %
+                                     (i, kd, stage, disp[i][1] if i < len(disp) else "end of trace"))
+                cur.append((stage,) + disp[i])
+                i += 1
+            if kinds == ("gemm",) and i < len(disp) and disp[i][0] == "reduce":
+                cur.append((stage,) + disp[i])
+                i += 1
+        if s >= warmup:
+            out.append(cur)
+    return out
+
+
+def counter_dispatches(prefix, counter):
+    """[(kind, name, value)] of library dispatches and the calibration factor
+    (bytes per counted KiB) of one counter run."""
+    by = collections.OrderedDict()
+    for r in csv.DictReader(open(prefix + "_counter_collection.csv")):
+        if r["Counter_Name"] != counter:
+            continue
+        d = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "v": 0.0})
+        d["v"] += float(r["Counter_Value"])
+    items = [d for _, d in sorted(by.items())]
+    cal = [d for d in items if "neg_kernel" in d["name"]]
+    if not cal:
+        raise SystemExit("%s: no calibration copy (run the bench with --copy-reference)" % prefix)
+    # the copy moves COPY_BYTES / 2 each way
+    factor = (COPY_BYTES / 2) / cal[-1]["v"]
+    return [(kernel_kind(d["name"]), short_name(d["name"]), d["v"]) for d in items if kernel_kind(d["name"])], factor
+
+
+def traffic(fetch_prefix, write_prefix, steps, warmup):
+    rd, fr = counter_dispatches(fetch_prefix, "FETCH_SIZE")
+    wr, fw = counter_dispatches(write_prefix, "WRITE_SIZE")
+    tr, tw = walk_steps(rd, steps, warmup), walk_steps(wr, steps, warmup)
+    per = collections.OrderedDict()
+    for sr, sw in zip(tr, tw):
+        stage_bytes = collections.OrderedDict()
+        for (stage, _, _, vr), (_, _, _, vw) in zip(sr, sw):
+            stage_bytes[stage] = stage_bytes.get(stage, 0.0) + vr * fr + vw * fw
+        for stage, b in stage_bytes.items():
+            per.setdefault(stage, []).append(b)
+    print("# stage  HBM bytes per launch (FETCH_SIZE x %.4f + WRITE_SIZE x %.4f, bytes per counted KiB)  "
+          "library source sha256" % (fr, fw))
+    digest = source_digest()
+    for stage, v in per.items():
+        print("%s %d %s" % (stage, round(sum(v) / len(v)), digest))
+
+
+def summarize(prefix, steps, warmup):
+    out = []
+    trace = prefix + "_kernel_trace.csv"
+    stats = prefix + "_kernel_stats.csv"
+    counters = prefix + "_counter_collection.csv"
+    if os.path.exists(stats):
+        out.append("## rocprofv3 --stats (whole run, all calls of each kernel)\n")
+        out.append("| kernel | calls | average us | min us | max us | share % |")
+        out.append("|---|---:|---:|---:|---:|---:|")
+        for r in csv.DictReader(open(stats)):
+            if kernel_kind(r["Name"]) is None:
+                continue
+            out.append("| %s | %s | %.1f | %.1f | %.1f | %.1f |" % (
+                short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        out.append("")
+    if os.path.exists(trace):
+        rows = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Dispatch_Id"]))
+        disp = [(kernel_kind(r["Kernel_Name"]), short_name(r["Kernel_Name"]),
+                 int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows
+                if kernel_kind(r["Kernel_Name"])]
+        timed = walk_steps(disp, steps, warmup)
+        per = collections.OrderedDict()
+        for st in timed:
+            for stage, kind, name, ns in st:
+                per.setdefault((stage, name), []).append(ns)
+        out.append("## timed steps, per stage (%d steps after %d warmup)\n" % (steps, warmup))
+        out.append("| stage | kernel | launches | average us | min us | max us |")
+        out.append("|---|---|---:|---:|---:|---:|")
+        for (stage, name), v in per.items():
+            out.append("| %s | %s | %d | %.1f | %.1f | %.1f |" % (stage, name, len(v), sum(v) / len(v) / 1e3,
+                                                                min(v) / 1e3, max(v) / 1e3))
+        step_us = [sum(x[3] for x in st) / 1e3 for st in timed]
+        out.append("\nsum of kernel durations per step: %.1f us (average over the timed steps)\n" %
+                   (sum(step_us) / len(step_us)))
+    if os.path.exists(counters):
+        by = collections.OrderedDict()
+        for r in csv.DictReader(open(counters)):
+            d = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": collections.Counter()})
+            d["c"][r["Counter_Name"]] += float(r["Counter_Value"])
+        items = sorted(by.items())
+        cal = [d for _, d in items if "neg_kernel" in d["name"]]
+        disp = [(kernel_kind(d["name"]), short_name(d["name"]), d["c"]) for _, d in items if kernel_kind(d["name"])]
+        timed = walk_steps(disp, steps, warmup)
+        names = sorted({k for _, _, c in disp for k in c})
+        out.append("## counters per dispatch (KiB for FETCH_SIZE / WRITE_SIZE), timed steps\n")
+        if cal:
+            c = cal[-1]["c"]
+            out.append("calibration: 512 MiB fp16 negation (reads 512 MiB, writes 512 MiB): " +
+                       ", ".join("%s = %.0f KiB -> factor %.4f" % (k, c[k], (COPY_BYTES / 2 / 1024) / c[k])
+                                 for k in names if c[k] > 0) + "\n")
+        out.append("| stage | kernel | " + " | ".join(names) + " |")
+        out.append("|---|---|" + "---:|" * len(names))
+        per = collections.OrderedDict()
+        for st in timed:
+            for stage, kind, name, c in st:
+                per.setdefault((stage, name), []).append(c)
+        for (stage, name), v in per.items():
+            out.append("| %s | %s | " % (stage, name) + " | ".join(
+                "%.0f" % (sum(x[k] for x in v) / len(v)) for k in names) + " |")
+        out.append("")
+    out.append("library source sha256: %s" % source_digest())
+    print("\n".join(out))
 
 
 def stage_times(fp8, torch, layers, reps):
@@ -85,13 +268,33 @@ def stage_times(fp8, torch, layers, reps):
     return res
 
 
+def measured_traffic(stage):
+    """HBM bytes per launch of `stage` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or None when
+    there is none for this stage or the library sources changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest()
+    for line in open(path):
+        f = line.split()
+        if line.startswith("#"):
+            continue
+        if len(f) == 3 and f[0] == stage and f[2] == digest:
+            return int(f[1])
+    return None
+
+
 def roofline_of(stage):
+    r = {"stage": stage["stage"], "launch_ms": round(stage["ms"], 4)}
     if "flops" in stage and stage["ai"] >= RIDGE:
-        return {"bound": "mfma", "achieved": round(stage["tflops"], 1), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(stage["tflops"] / FP8_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": stage["stage"]}
-    return {"bound": "hbm", "achieved": round(stage["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(stage["gbs"] / HBM_PEAK_GBS, 4), "traffic": None, "kernel": stage["stage"]}
+        r.update({"bound": "mfma", "achieved": round(stage["tflops"], 1), "peak": FP8_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": round(stage["tflops"] / FP8_PEAK_TFLOPS, 4)})
+    else:
+        r.update({"bound": "hbm", "achieved": round(stage["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(stage["gbs"] / HBM_PEAK_GBS, 4)})
+    r["traffic"] = measured_traffic(stage["stage"])
+    return r
 
 
 def cpu_baseline(shapes, tokens):
@@ -116,6 +319,12 @@ def cpu_baseline(shapes, tokens):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, args.steps, args.warmup)
+        return
+    if args.traffic:
+        traffic(args.traffic[0], args.traffic[1], args.steps, args.warmup)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
@@ -128,7 +337,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     N = args.tokens
-    shapes = [(512, 2048), (2048, 512)]
+    shapes = SHAPES
     layers = []
     for idx, (K, M) in enumerate(shapes):
         x, w, dy = synth.operands_on_device(N, K, M, seed=idx, device=dev)
@@ -159,6 +368,15 @@ def main():
     value = flops / (ms / 1e3) / 1e12
     print("timed %d steps: %.4f ms/step (wall %.3f s)" % (args.steps, ms, wall), file=sys.stderr, flush=True)
 
+    if args.copy_reference:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.no_breakdown:
+        print(json.dumps({"ms_per_step": round(ms, 4), "value": round(value, 2)}), flush=True)
+        return
     stages = stage_times(fp8, torch, layers, args.reps)
     for s in stages:
         print("  %-24s %8.4f ms  %s" % (s["stage"], s["ms"],
@@ -166,7 +384,7 @@ def main():
                                         else "%.0f GB/s" % s["gbs"]), file=sys.stderr, flush=True)
     q = [s for s in stages if s["stage"].startswith("quant")]
     quant_gbs = sum(s["bytes"] for s in q) / sum(s["ms"] for s in q) / 1e6
-    dom = max(stages, key=lambda s: s["ms"])
+    dom = max(stages, key=lambda s: s["ms"])     # the stage (one library call) that takes longest
     pages_tflops = sum(6 * 131072 * K * M for K, M in shapes) / (sum(PAGES_MS[s] for s in shapes) / 1e3) / 1e12
 
     out = {
