@@ -64,7 +64,7 @@ def parse():
 
 SHAPES = [(512, 2048), (2048, 512)]
 KINDS = (("amax_partial_kernel", "amax"), ("cast_kernel", "cast"), ("gemm_kernel", "gemm"),
-         ("splitk_reduce_kernel", "reduce"))
+         ("gemm_tensor_kernel", "gemm"), ("splitk_reduce_kernel", "reduce"))
 COPY_BYTES = 2 * 512 * 1024 * 1024      # the --copy-reference kernel reads 512 MiB and writes 512 MiB
 
 
@@ -81,14 +81,16 @@ def step_sequence(shapes):
 
 
 def kernel_kind(name):
+    if "fp8k::" not in name:
+        return None
     for key, kind in KINDS:
-        if "fp8k::" + key in name:
+        if "::" + key + "<" in name or "::" + key + "(" in name:
             return kind
     return None
 
 
 def short_name(name):
-    return name.replace("void ", "").replace("fp8k::", "")
+    return name.replace("void ", "").replace("fp8k::", "").replace("tensor::", "")
 
 
 def source_digest():

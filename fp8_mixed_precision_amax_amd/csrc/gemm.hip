@@ -1,55 +1,50 @@
-// FP8 GEMM C[i][j] = sum_k A[i][k] B[j][k] on the gfx950 FP8 matrix cores.
+// Block-scaled FP8 GEMM C[i][j] = sum_kb (sA[i][kb] sB[j][kb]) sum_{k in kb}
+// A[i][k] B[j][k] on the gfx950 FP8 matrix cores, the split-K reduction shared
+// with the tensorwise kernel, and the GEMM dispatcher.
 //
 // Method ("Native FP8 MLP reconstruction", implementation paragraph): the
 // three GEMMs of the FP8 linear take FP8 operands (E4M3 x E4M3 forward,
 // E5M2 x E4M3 for both gradients), accumulate at full fp32 precision (no
-// fast accumulation) and write BF16.  Tensorwise scales are applied once in
-// the epilogue; block scales (Float8BlockScaling, TransformerEngine issue
-// 2852) are applied to every 128-long contraction block's partial sum, which
-// is then added to an fp32 accumulator.
+// fast accumulation) and write BF16.  Block scales (Float8BlockScaling,
+// TransformerEngine issue 2852) are applied to every 128-long contraction
+// block's partial sum, which is then added to an fp32 accumulator.  The
+// tensorwise GEMM (one scale pair, applied in the epilogue) lives in
+// gemm_tensor.hip.
 //
-// Design (one kernel for all three GEMMs: every operand is contraction-
-// contiguous, "NT"):
+// Design of the block-scaled kernel (every operand contraction-contiguous):
 //  - persistent: one workgroup per CU walks a list of work items (output tile,
 //    split-K slice); the software pipeline runs continuously across item
 //    boundaries, so the next tile's first K stages stream in while the
 //    current tile's epilogue stores go out.
 //  - workgroup 256 threads = 4 waves in 2x2, output tile 256x128 (wave tile
-//    128x64 = 4x2 v_mfma_f32_32x32x64_f8f6f4 blocks).  Tensorwise: BK=64, 2 LDS
-//    stages, two workgroups per CU (their loops interleave on each SIMD);
-//    block-scaled: BK=128 (one scale block per K step), 3 stages, one
-//    workgroup per CU (per-block fp32 promotion keeps the accumulators and
-//    the block partial sums in VGPRs).
+//    128x64 = 4x2 v_mfma_f32_32x32x64_f8f6f4 blocks), BK=128 (one scale block
+//    per K step), 3 LDS stages; per-block fp32 promotion keeps the
+//    accumulators and the block partial sums in VGPRs.
 //  - operands move HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging):
 //    each instruction fills 1 KiB of LDS at M0 + 16 * lane; the lane picks
 //    its global 16-byte chunk so that the LDS rows come out XOR-swizzled
 //    (16-byte chunk index ^ f(row)), which makes the fragment reads of 16
-//    consecutive rows hit 16 distinct bank groups.
+//    consecutive rows hit 16 distinct bank groups.  The stage also carries
+//    the fp32 factors of its 128-block (4-byte LDS-DMA).
 //  - stage hand-off: each wave waits with s_waitcnt vmcnt(n) for its own
 //    loads of the stage, then a plain s_barrier (no fence: a workgroup
 //    release fence would force vmcnt(0) and drain the prefetch queue).
 //  - the B tile is the matrix cores' "A" operand, so each lane's accumulators
-//    hold one output row i and runs of 4 consecutive columns j.  Tensorwise
-//    epilogue: each wave converts 32 rows at a time to bf16 into its own LDS
-//    slice and stores them back as whole 128-byte row segments (16 bytes per
-//    lane); the 8-byte register-layout stores touch 32 rows per instruction
-//    and write at less than half the HBM rate.
+//    hold one output row i and runs of 4 consecutive columns j, stored as
+//    8-byte bf16 runs.
 //  - work items are dealt so that the workgroups on one XCD (the dispatcher
 //    deals workgroups round-robin over the 8 XCDs) take consecutive items,
-//    rastered in groups of 8 tile-rows for L2 reuse of A.
+//    rastered in groups of 8 tile rows for L2 reuse of A.
 //  - split-K (small outputs with long contractions, e.g. the weight
 //    gradient): each slice writes fp32 partials; a reduce kernel sums the
 //    slices in fixed order (deterministic), applies the tensorwise factor and
 //    rounds to bf16.
 #include <type_traits>
 
+#include "gemm_common.hpp"
 #include "internal.hpp"
 
 namespace fp8k {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
@@ -63,7 +58,6 @@ struct GemmCfg {
     static_assert(BM == 256 && BN == 2 * WNJ * 32, "4 waves in 2 x 2, wave tile 128 x 32*WNJ");
     static_assert(BK == 64 || BK == 128, "BK");
 };
-using CfgTensor = GemmCfg<256, 128, 64, 2, 2, 2, 1>;
 using CfgBlock = GemmCfg<256, 128, 128, 3, 2, 1>;
 
 struct GemmArgs {
@@ -79,18 +73,6 @@ struct GemmArgs {
     int items;        // tiles_i * tiles_j * splits
 };
 
-template <int FA, int FB>
-__device__ __forceinline__ v16f mfma(const v8i& bfrag, const v8i& afrag, const v16f& c) {
-    // matrix-core operand 0 = B fragment (rows j), operand 1 = A fragment (rows i)
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfrag, afrag, c, FB, FA, 0, 0, 0, 0);
-}
-
-// XOR swizzle of the 16-byte chunk index of an LDS row
-template <int BK>
-__device__ __forceinline__ int swz(int row) {
-    return BK == 64 ? ((row >> 2) & 3) : ((row >> 1) & 7);
-}
-
 // 32 bytes of LDS row `row` (logical 16-byte chunks c0, c0 + 1)
 template <int BK>
 __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int c0) {
@@ -98,17 +80,6 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int c0) {
     const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * BK + ((c0 ^ s) << 4));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + row * BK + (((c0 + 1) ^ s) << 4));
     return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-__device__ __forceinline__ void barrier_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// s_waitcnt vmcnt(n) for n in 0..63 (gfx9 encoding: low 4 bits + bits 15:14;
-// expcnt and lgkmcnt fields left at "no wait")
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 struct Item {
@@ -516,11 +487,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
-static int block_n(bool block) { return block ? CfgBlock::BN : CfgTensor::BN; }
-static int block_k(bool block) { return block ? CfgBlock::BK : CfgTensor::BK; }
-static int block_occ(bool block) { return block ? CfgBlock::OCC : CfgTensor::OCC; }
-
-static int cu_count() {
+int cu_count() {
     static int cache[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -533,11 +500,12 @@ static int cu_count() {
 }
 
 int gemm_splits(int64_t I, int64_t J, int64_t K, bool block) {
-    const int64_t tiles = ((I + 255) / 256) * ((J + block_n(block) - 1) / block_n(block));
+    if (!block) return gemm_tensor_splits(I, J, K);
+    const int64_t tiles = ((I + CfgBlock::BM - 1) / CfgBlock::BM) * ((J + CfgBlock::BN - 1) / CfgBlock::BN);
     const int64_t k128 = K / 128;
     // aim for one work item per resident workgroup (256 CUs x occupancy),
     // keep >= 8 blocks of 128 per split
-    const int64_t slots = 256 * block_occ(block);
+    const int64_t slots = 256 * CfgBlock::OCC;
     int64_t s = 1;
     while (tiles * s < slots && k128 / (s * 2) >= 8 && s < 64) s *= 2;
     return (int)s;
@@ -551,39 +519,44 @@ size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K) {
 
 hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream) {
     const bool block = l.sa.group != 0;
-    const int bn = block_n(block);
-    GemmArgs g;
-    g.a = static_cast<const uint8_t*>(l.a);
-    g.b = static_cast<const uint8_t*>(l.b);
-    g.sa = l.sa;
-    g.sb = l.sb;
-    g.I = l.I;
-    g.J = l.J;
-    g.K = l.K;
-    g.c = static_cast<uint16_t*>(l.c);
-    g.part = static_cast<float*>(l.ws);
-    g.splits = gemm_splits(l.I, l.J, l.K, block);
-    g.tiles_i = (int)((l.I + 255) / 256);
-    g.tiles_j = (int)((l.J + bn - 1) / bn);
-    g.ktiles = (int)(l.K / block_k(block));
-    g.items = g.tiles_i * g.tiles_j * g.splits;
-    int grid = cu_count() * block_occ(block);
-    if (grid > g.items) grid = g.items;
-#define FP8K_GEMM(FA, FB, BL) \
-    hipLaunchKernelGGL((gemm_kernel<FA, FB, BL, typename std::conditional<BL, CfgBlock, CfgTensor>::type>), \
-                       dim3(grid), dim3(kThreads), 0, stream, g)
-    if (l.fa == 0 && l.fb == 0) { if (block) FP8K_GEMM(0, 0, true); else FP8K_GEMM(0, 0, false); }
-    else if (l.fa == 1 && l.fb == 0) { if (block) FP8K_GEMM(1, 0, true); else FP8K_GEMM(1, 0, false); }
-    else if (l.fa == 0 && l.fb == 1) { if (block) FP8K_GEMM(0, 1, true); else FP8K_GEMM(0, 1, false); }
-    else { if (block) FP8K_GEMM(1, 1, true); else FP8K_GEMM(1, 1, false); }
+    const int splits = gemm_splits(l.I, l.J, l.K, block);
+    if (!block) {
+        hipError_t e = launch_gemm_tensor(l, splits, stream);
+        if (e != hipSuccess || splits == 1) return e;
+    } else {
+        GemmArgs g;
+        g.a = static_cast<const uint8_t*>(l.a);
+        g.b = static_cast<const uint8_t*>(l.b);
+        g.sa = l.sa;
+        g.sb = l.sb;
+        g.I = l.I;
+        g.J = l.J;
+        g.K = l.K;
+        g.c = static_cast<uint16_t*>(l.c);
+        g.part = static_cast<float*>(l.ws);
+        g.splits = splits;
+        g.tiles_i = (int)((l.I + CfgBlock::BM - 1) / CfgBlock::BM);
+        g.tiles_j = (int)((l.J + CfgBlock::BN - 1) / CfgBlock::BN);
+        g.ktiles = (int)(l.K / CfgBlock::BK);
+        g.items = g.tiles_i * g.tiles_j * g.splits;
+        int grid = cu_count() * CfgBlock::OCC;
+        if (grid > g.items) grid = g.items;
+#define FP8K_GEMM(FA, FB) \
+    hipLaunchKernelGGL((gemm_kernel<FA, FB, true, CfgBlock>), dim3(grid), dim3(kThreads), 0, stream, g)
+        if (l.fa == 0 && l.fb == 0) FP8K_GEMM(0, 0);
+        else if (l.fa == 1 && l.fb == 0) FP8K_GEMM(1, 0);
+        else if (l.fa == 0 && l.fb == 1) FP8K_GEMM(0, 1);
+        else FP8K_GEMM(1, 1);
 #undef FP8K_GEMM
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || g.splits == 1) return e;
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || splits == 1) return e;
+    }
     const int64_t n4 = l.I * l.J / 4;
     int64_t blocks = (n4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       (const float*)g.part, g.splits, n4, l.I * l.J, l.sa.sinv, l.sb.sinv, block ? 0 : 1, g.c);
+                       static_cast<const float*>(l.ws), splits, n4, l.I * l.J, l.sa.sinv, l.sb.sinv, block ? 0 : 1,
+                       static_cast<uint16_t*>(l.c));
     return hipGetLastError();
 }
 

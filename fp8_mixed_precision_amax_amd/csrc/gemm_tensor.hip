@@ -1,0 +1,374 @@
+// Tensorwise-scaled FP8 GEMM C[i][j] = t * sum_k A[i][k] B[j][k] on the gfx950
+// matrix cores (t = product of the two operands' inverse scales, applied once
+// in the epilogue; BF16 output, or fp32 partial sums for split-K).
+//
+// Method ("Native FP8 MLP reconstruction", implementation paragraph): the
+// three GEMMs of the FP8 linear (E4M3 x E4M3 forward, E5M2 x E4M3 for both
+// gradients) accumulate at full fp32 precision across the contraction and
+// write BF16.  Every operand is contraction-contiguous ("NT").
+//
+// Design
+//  - persistent: one workgroup per CU walks work items (256 x 256 output
+//    tile, split-K slice) dealt XCD by XCD (the dispatcher puts workgroup b on
+//    XCD b % 8) and rastered in groups of 8 tile rows, so the workgroups of one
+//    XCD share A and B tiles through its L2.
+//  - 8 waves, two per SIMD, wave tile 128 x 64 (4 x 2 blocks of
+//    v_mfma_f32_32x32x64_f8f6f4, 128 accumulator registers), all waves in
+//    lock step with one s_barrier per 64-long contraction step.
+//  - operands stream HBM -> LDS with buffer_load ... lds (LDS-DMA, no VGPR
+//    staging): 4 stages of 32 KiB, 3 in flight; each wave moves 4 KiB per
+//    stage through a buffer resource based at the tile (rows past I or J lie
+//    outside the resource and read as zero).  LDS rows are XOR-swizzled.
+//  - per step, after the barrier, a wave issues the DMA of the stage three
+//    ahead, then its 8 MFMAs with the fragments of the next step read in
+//    between (A fragment mi is reloaded right after its last MFMA; the two B
+//    fragments alternate between two register sets).
+//  - the hand-off of a stage is one s_waitcnt vmcnt(n) on the wave's own DMA
+//    (n counted exactly: the loads and epilogue stores issued after it) plus
+//    the barrier; fragment reads are inline assembly so the compiler adds no
+//    vmcnt(0) in front of them.
+//  - epilogue: each wave converts 32 rows at a time to bf16 into a private
+//    4 KiB LDS slice (chunk-major, (row ^ 2 chunk) swizzle: conflict-free
+//    writes and reads) and stores whole 128-byte row segments.
+#include "gemm_common.hpp"
+#include "internal.hpp"
+
+namespace fp8k {
+namespace tensor {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int S = 4;                      // LDS stages (power of two)
+constexpr int D = S - 1;                  // stages in flight ahead of the one read
+constexpr int NW = 8;                     // waves
+constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
+constexpr int LA = A_BYTES / 1024 / NW;   // LDS-DMA instructions per wave per stage (A)
+constexpr int LB = B_BYTES / 1024 / NW;   // (B)
+constexpr int L = LA + LB;
+constexpr int RPK = 1024 / BK;            // rows per 1 KiB DMA block
+constexpr int CPR = BK / 16;              // 16-byte chunks per LDS row
+constexpr int ECH = 8;                    // 16-byte chunks per epilogue row (64 bf16)
+constexpr int SLICE = 32 * ECH * 16;      // per-wave epilogue slice
+static_assert(S * STAGE + NW * SLICE <= 160 * 1024, "LDS");
+static_assert((S & (S - 1)) == 0, "S");
+
+struct Args {
+    const uint8_t* a;
+    const uint8_t* b;
+    const float* sa;      // tensorwise inverse scales
+    const float* sb;
+    int64_t I, J, K;
+    uint16_t* c;
+    float* part;          // split-K partials [splits][I][J]
+    int splits, tiles_i, tiles_j, kpairs, items;
+};
+
+struct Item {
+    int ti, tj, z, kb, ke;   // kb, ke: contraction steps of BK (even)
+};
+
+__device__ __forceinline__ bool item_at(const Args& g, int r, Item& it) {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int Lg = r * G + ((G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b);
+    if (Lg >= g.items) return false;
+    const int tiles = g.tiles_i * g.tiles_j;
+    const int z = Lg / tiles, t = Lg - z * tiles;
+    constexpr int GI = 8;
+    const int per_group = GI * g.tiles_j, grp = t / per_group, local = t - grp * per_group;
+    int rows = g.tiles_i - grp * GI;
+    rows = rows < GI ? rows : GI;
+    it.ti = grp * GI + local % rows;
+    it.tj = local / rows;
+    it.z = z;
+    // slices in units of 128 (two steps), so every item has an even count
+    it.kb = 2 * (int)(((int64_t)g.kpairs * z) / g.splits);
+    it.ke = 2 * (int)(((int64_t)g.kpairs * (z + 1)) / g.splits);
+    return true;
+}
+
+// s_waitcnt vmcnt(n) for a runtime n (rounded down to a supported value)
+__device__ __forceinline__ void wait_vm_n(int n) {
+    if (n == L) wait_vm<L>();
+    else if (n >= 63) wait_vm<63>();
+    else if (n >= 48) wait_vm<48>();
+    else if (n >= 32) wait_vm<32>();
+    else if (n >= 24) wait_vm<24>();
+    else if (n >= 16) wait_vm<16>();
+    else if (n >= 8) wait_vm<8>();
+    else if (n >= 4) wait_vm<4>();
+    else wait_vm<0>();
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
+    // separate objects: the epilogue's LDS traffic never aliases the stages
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sepi[NW * SLICE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int wi = wave & 1, wj = wave >> 1;
+    const uint32_t K = (uint32_t)g.K;
+    const uint32_t K16 = K * RPK;
+
+    // ---- load cursor (uniform) ---------------------------------------------
+    int l_round = 0;
+    Item l_it;
+    bool l_ok = item_at(g, 0, l_it);
+    __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, 0);
+    __amdgpu_buffer_rsrc_t rb = ra;
+    // lane offset inside a 16-row DMA block: row lane/4, swizzled chunk
+    const uint32_t loff = (uint32_t)(lane / CPR) * K + (uint32_t)(((lane % CPR) ^ swz<BK>(lane / CPR)) * 16);
+    const uint32_t wrow_off = (uint32_t)(wave * LA * RPK) * K;   // this wave's first row of the tile
+    uint32_t l_so = 0;   // buffer offset of the next stage to load
+    int l_left = 0;      // stages left in the load item
+    auto set_load_item = [&]() __attribute__((always_inline)) {
+        const int64_t i0 = (int64_t)l_it.ti * BM, j0 = (int64_t)l_it.tj * BN;
+        ra = make_rsrc(g.a + i0 * g.K, (g.I - i0 < BM ? g.I - i0 : BM) * g.K);
+        rb = make_rsrc(g.b + j0 * g.K, (g.J - j0 < BN ? g.J - j0 : BN) * g.K);
+        l_so = wrow_off + (uint32_t)l_it.kb * BK;
+        l_left = l_it.ke - l_it.kb;
+    };
+    if (l_ok) set_load_item();
+    const uint32_t smem0 = lds_off(smem);
+    uint32_t dma_off = 0;   // stage buffer the next DMA fills
+    auto issue_stage = [&]() __attribute__((always_inline)) {
+        const uint32_t dA = smem0 + dma_off + (uint32_t)(wave * LA * 1024);
+        const uint32_t dB = smem0 + dma_off + (uint32_t)(A_BYTES + wave * LB * 1024);
+#pragma unroll
+        for (int p = 0; p < LA; p++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(uintptr_t)(dA + p * 1024),
+                                                     16, loff, __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * K16), 0, 0);
+#pragma unroll
+        for (int p = 0; p < LB; p++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(uintptr_t)(dB + p * 1024),
+                                                     16, loff, __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * K16), 0, 0);
+        dma_off = (dma_off + STAGE) & (S * STAGE - 1);
+        l_so += BK;
+        if (--l_left == 0) {
+            if (l_ok && item_at(g, l_round + 1, l_it)) {
+                l_round++;
+                set_load_item();
+            } else {
+                // past the last item: keep re-reading its last stage into
+                // buffers nobody reads, so every step issues the same loads
+                l_ok = false;
+                l_so -= BK;
+                l_left = 1;
+            }
+        }
+    };
+
+    // ---- prologue: D stages in flight, stage 0 landed, its fragments read --
+#pragma unroll
+    for (int s = 0; s < D; s++) issue_stage();
+    wait_vm<(D - 1) * L>();
+    barrier_lds();
+
+    int c_round = 0;
+    Item c_it;
+    bool c_ok = item_at(g, 0, c_it);
+    int st_cur = 0;   // epilogue stores issued since the last stage wait
+
+    const int frow = lane & 31;
+    const int arow = wi * 128 + frow, brow = wj * 64 + frow;
+    const int ch = (lane >> 5) * 2;
+    const float t_tensor = g.sa[0] * g.sb[0];
+    // fragment rows in a stage: chunk ch (and ch+1 at ^16), +2048 per 32 rows
+    const uint32_t offA = (uint32_t)(arow * BK + ((ch ^ swz<BK>(arow)) << 4));
+    const uint32_t offB = (uint32_t)(A_BYTES + brow * BK + ((ch ^ swz<BK>(brow)) << 4));
+
+    v16f acc[4][2];
+    v8i fa[4], fb0[2], fb1[2];
+#pragma unroll
+    for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+        for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[mi][nj][v] = 0.0f;
+    {
+        const uint32_t a0 = smem0 + offA, a1 = a0 ^ 16u, b0 = smem0 + offB, b1 = b0 ^ 16u;
+        fa[0] = ds_frag<0>(a0, a1);
+        fa[1] = ds_frag<2048>(a0, a1);
+        fa[2] = ds_frag<4096>(a0, a1);
+        fa[3] = ds_frag<6144>(a0, a1);
+        fb0[0] = ds_frag<0>(b0, b1);
+        fb0[1] = ds_frag<2048>(b0, b1);
+    }
+    uint32_t rd_off = STAGE;   // stage buffer of the next fragments
+
+    // epilogue slice: (row r, chunk c) at c*512 + ((r ^ 2c) << 4)
+    const uint32_t slice = lds_off(sepi) + (uint32_t)(wave * SLICE);
+    const uint32_t wbase = slice + (uint32_t)((lane >> 5) * 8);
+    const uint32_t rc = (uint32_t)(lane & 7), rr = (uint32_t)(lane >> 3);
+    const uint32_t goff = (uint32_t)(rr * (uint32_t)g.J * 2 + rc * 16);
+
+    // write one item's accumulators; returns the vector-memory stores issued
+    auto epilogue = [&](const Item& it) __attribute__((always_inline)) -> int {
+        const int64_t i0 = (int64_t)it.ti * BM, j0 = (int64_t)it.tj * BN;
+        const int64_t jw = j0 + wj * 64;
+        // validity is uniform per wave (I and J are multiples of 128)
+        if (!((i0 + wi * 128 < g.I) && (jw < g.J))) return 0;
+        if (g.splits > 1) {
+            float* out = g.part + (int64_t)it.z * g.I * g.J + (i0 + arow) * g.J + jw + 4 * (lane >> 5);
+#pragma unroll
+            for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+                for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        *reinterpret_cast<float4*>(out + (int64_t)mi * 32 * g.J + nj * 32 + 8 * q) =
+                            make_float4(acc[mi][nj][4 * q], acc[mi][nj][4 * q + 1], acc[mi][nj][4 * q + 2],
+                                        acc[mi][nj][4 * q + 3]);
+            return 4 * 2 * 4;
+        }
+        uint8_t* out_base = reinterpret_cast<uint8_t*>(g.c + (i0 + wi * 128) * g.J + jw);
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++) {
+#pragma unroll
+            for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const __bf16 h0 = (__bf16)(acc[mi][nj][4 * q] * t_tensor);
+                    const __bf16 h1 = (__bf16)(acc[mi][nj][4 * q + 1] * t_tensor);
+                    const __bf16 h2 = (__bf16)(acc[mi][nj][4 * q + 2] * t_tensor);
+                    const __bf16 h3 = (__bf16)(acc[mi][nj][4 * q + 3] * t_tensor);
+                    uint2 w;
+                    w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                    w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                    const int chunk = nj * 4 + q;
+                    const uint32_t wa = wbase + (uint32_t)(chunk * 512 + ((frow ^ (2 * chunk)) << 4));
+                    asm volatile("ds_write_b64 %0, %1" : : "v"(wa), "v"(w) : "memory");
+                }
+            // a wave's LDS operations execute in order: the read-back sees the
+            // writes above, and the next block's writes follow these reads
+            u32x4 r0, r1, r2, r3;
+            const uint32_t ra0 = slice + rc * 512 + ((rr ^ (2 * rc)) << 4);
+            const uint32_t ra1 = slice + rc * 512 + (((rr + 8) ^ (2 * rc)) << 4);
+            const uint32_t ra2 = slice + rc * 512 + (((rr + 16) ^ (2 * rc)) << 4);
+            const uint32_t ra3 = slice + rc * 512 + (((rr + 24) ^ (2 * rc)) << 4);
+            asm volatile("ds_read_b128 %0, %1" : "=v"(r0) : "v"(ra0) : "memory");
+            asm volatile("ds_read_b128 %0, %1" : "=v"(r1) : "v"(ra1) : "memory");
+            asm volatile("ds_read_b128 %0, %1" : "=v"(r2) : "v"(ra2) : "memory");
+            asm volatile("ds_read_b128 %0, %1" : "=v"(r3) : "v"(ra3) : "memory");
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0), "+v"(r1), "+v"(r2), "+v"(r3));
+            uint8_t* ob = out_base + (int64_t)mi * 32 * g.J * 2;
+            *reinterpret_cast<u32x4*>(ob + goff) = r0;
+            *reinterpret_cast<u32x4*>(ob + (int64_t)8 * g.J * 2 + goff) = r1;
+            *reinterpret_cast<u32x4*>(ob + (int64_t)16 * g.J * 2 + goff) = r2;
+            *reinterpret_cast<u32x4*>(ob + (int64_t)24 * g.J * 2 + goff) = r3;
+        }
+        return 4 * 4;
+    };
+
+    // One contraction step.  Stage k+1 (whose fragments this step reads) must
+    // have landed everywhere: wait for this wave's DMA of it -- the ops issued
+    // after it are the DMA of stage k+2 and any epilogue stores since -- then
+    // the barrier, which also retires every wave's reads of the buffer the
+    // DMA below overwrites (stage k-1's).
+#define FP8K_MF(MI, FBC, FIRST)                                                                    \
+    do {                                                                                           \
+        acc[MI][0] = mfma<FA, FB>(FBC[0], fa[MI], (FIRST) ? vzero : acc[MI][0]);                  \
+        acc[MI][1] = mfma<FA, FB>(FBC[1], fa[MI], (FIRST) ? vzero : acc[MI][1]);                  \
+    } while (0)
+#define FP8K_STEP(FBC, FBN, FIRST)                                                                 \
+    do {                                                                                           \
+        wait_vm_n(L + st_cur);                                                                     \
+        st_cur = 0;                                                                                \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"                                           \
+                     : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(FBC[0]), "+v"(FBC[1]) \
+                     :                                                                             \
+                     : "memory");                                                                  \
+        issue_stage();                                                                             \
+        const uint32_t sb_ = smem0 + rd_off;                                                       \
+        rd_off = (rd_off + STAGE) & (S * STAGE - 1);                                               \
+        const uint32_t a0_ = sb_ + offA, a1_ = a0_ ^ 16u, b0_ = sb_ + offB, b1_ = b0_ ^ 16u;       \
+        FP8K_MF(0, FBC, FIRST);                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        fa[0] = ds_frag<0>(a0_, a1_);                                                              \
+        FBN[0] = ds_frag<0>(b0_, b1_);                                                             \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        FP8K_MF(1, FBC, FIRST);                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        fa[1] = ds_frag<2048>(a0_, a1_);                                                           \
+        FBN[1] = ds_frag<2048>(b0_, b1_);                                                          \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        FP8K_MF(2, FBC, FIRST);                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        fa[2] = ds_frag<4096>(a0_, a1_);                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        FP8K_MF(3, FBC, FIRST);                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        fa[3] = ds_frag<6144>(a0_, a1_);                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+    } while (0)
+
+    const v16f vzero = {};
+    bool have_prev = false;
+    Item p_it;
+    while (c_ok) {
+        Item n_it;
+        const bool more = item_at(g, c_round + 1, n_it);
+        const int nsteps = c_it.ke - c_it.kb;   // even, >= 2
+        if (have_prev) st_cur += epilogue(p_it);
+        FP8K_STEP(fb0, fb1, true);
+        for (int s = 1; s < nsteps - 1; s += 2) {
+            FP8K_STEP(fb1, fb0, false);
+            FP8K_STEP(fb0, fb1, false);
+        }
+        // after the last item the fragments this reads are unused (their
+        // stage is a re-read of the last one); reading anyway keeps a single
+        // definition of every fragment register
+        FP8K_STEP(fb1, fb0, false);
+        p_it = c_it;
+        have_prev = true;
+        c_it = n_it;
+        c_ok = more;
+        c_round++;
+    }
+#undef FP8K_STEP
+#undef FP8K_MF
+    if (have_prev) epilogue(p_it);
+    wait_vm<0>();
+}
+
+}  // namespace tensor
+
+using namespace tensor;
+
+int gemm_tensor_splits(int64_t I, int64_t J, int64_t K) {
+    const int64_t tiles = ((I + BM - 1) / BM) * ((J + BN - 1) / BN);
+    const int64_t kp = K / 128;
+    // aim for one work item per CU, keep >= 8 blocks of 128 per slice
+    int64_t s = 1;
+    while (tiles * s < 256 && kp / (s * 2) >= 8 && s < 64) s *= 2;
+    return (int)s;
+}
+
+hipError_t launch_gemm_tensor(const GemmLaunch& l, int splits, hipStream_t stream) {
+    Args g;
+    g.a = static_cast<const uint8_t*>(l.a);
+    g.b = static_cast<const uint8_t*>(l.b);
+    g.sa = l.sa.sinv;
+    g.sb = l.sb.sinv;
+    g.I = l.I;
+    g.J = l.J;
+    g.K = l.K;
+    g.c = static_cast<uint16_t*>(l.c);
+    g.part = static_cast<float*>(l.ws);
+    g.splits = splits;
+    g.tiles_i = (int)((l.I + BM - 1) / BM);
+    g.tiles_j = (int)((l.J + BN - 1) / BN);
+    g.kpairs = (int)(l.K / 128);
+    g.items = g.tiles_i * g.tiles_j * splits;
+    int grid = cu_count();
+    if (grid > g.items) grid = g.items;
+#define FP8K_LAUNCH(FA, FB) \
+    hipLaunchKernelGGL((gemm_tensor_kernel<FA, FB>), dim3(grid), dim3(NW * 64), 0, stream, g)
+    if (l.fa == 0 && l.fb == 0) FP8K_LAUNCH(0, 0);
+    else if (l.fa == 1 && l.fb == 0) FP8K_LAUNCH(1, 0);
+    else if (l.fa == 0 && l.fb == 1) FP8K_LAUNCH(0, 1);
+    else FP8K_LAUNCH(1, 1);
+#undef FP8K_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace fp8k
