@@ -313,6 +313,21 @@ def _gemm_operands_wgrad(dyq, xq, scaling, N, K, M):
             xq["q_col"], BlockScale(xq["scale_inv_col"], 1, N // 128, 1))
 
 
+def fprop_operands(xq, wq, scaling, N, K, M):
+    """(A, sA, B, sB) of Y = X W^T as gemm_block / gemm_block_sampled take them."""
+    return _gemm_operands_fprop(xq, wq, scaling, N, K, M)
+
+
+def dgrad_operands(dyq, wq, scaling, N, K, M):
+    """(A, sA, B, sB) of dX = dY W."""
+    return _gemm_operands_dgrad(dyq, wq, scaling, N, K, M)
+
+
+def wgrad_operands(dyq, xq, scaling, N, K, M):
+    """(A, sA, B, sB) of dW = dY^T X."""
+    return _gemm_operands_wgrad(dyq, xq, scaling, N, K, M)
+
+
 def _gemm(a, fa, sa, b, fb, sb, scaling):
     if scaling == "tensor":
         return gemm_tensor(a, fa, b, fb, sa.s[0], sb.s[0])

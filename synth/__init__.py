@@ -30,15 +30,15 @@ WORKLOADS = {
 }
 
 
-def normal_bf16(shape, sigma, gen, outlier_frac=0.0, outlier_factor=100.0):
+def normal_bf16(shape, sigma, gen, outlier_frac=0.0, outlier_factor=100.0, device="cpu"):
     """fp32 N(0, sigma^2) draws rounded to bf16; with outlier_frac > 0 a
     Bernoulli(outlier_frac) mask drawn next from the same generator selects
     entries multiplied by outlier_factor before the bf16 rounding."""
-    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    x = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
     if sigma != 1.0:
         x.mul_(sigma)
     if outlier_frac > 0.0:
-        mask = torch.rand(shape, generator=gen, dtype=torch.float32) < outlier_frac
+        mask = torch.rand(shape, generator=gen, dtype=torch.float32, device=device) < outlier_frac
         x[mask] *= outlier_factor
     return x.to(torch.bfloat16)
 
@@ -70,13 +70,21 @@ def sha256(t):
     return hashlib.sha256(bits(t).tobytes()).hexdigest()
 
 
-def operands_on_device(N, K, M, seed=0, sigma_x=1.0, sigma_w=0.02, sigma_dy=1e-3, device="cuda"):
+def operands_on_device(N, K, M, seed=0, sigma_x=1.0, sigma_w=0.02, sigma_dy=1e-3, device="cuda",
+                       outlier_frac=0.0):
     """Same distributions as ``operands`` drawn with a seeded device generator
-    (for large timing runs where CPU drawing would dominate); drawn in the
-    order X, W, dY."""
+    (for large runs where CPU drawing would dominate); drawn in the order
+    X, W, dY."""
     g = torch.Generator(device=device)
     g.manual_seed(seed)
-    x = (torch.randn((N, K), generator=g, device=device, dtype=torch.float32) * sigma_x).to(torch.bfloat16)
-    w = (torch.randn((M, K), generator=g, device=device, dtype=torch.float32) * sigma_w).to(torch.bfloat16)
-    dy = (torch.randn((N, M), generator=g, device=device, dtype=torch.float32) * sigma_dy).to(torch.bfloat16)
+    x = normal_bf16((N, K), sigma_x, g, outlier_frac, device=device)
+    w = normal_bf16((M, K), sigma_w, g, outlier_frac, device=device)
+    dy = normal_bf16((N, M), sigma_dy, g, outlier_frac, device=device)
     return x, w, dy
+
+
+def workload_on_device(name, seed=0, device="cuda"):
+    """A named workload drawn with the seeded device generator."""
+    N, K, M, sx, sw, sdy, frac, scaling = WORKLOADS[name]
+    x, w, dy = operands_on_device(N, K, M, seed, sx, sw, sdy, device, frac)
+    return {"x": x, "w": w, "dy": dy, "N": N, "K": K, "M": M, "scaling": scaling}

@@ -93,3 +93,19 @@ def check_bf16(got_bits, ref_bits, Kc, name="", hw=None):
     assert fro <= 1e-2, (name, rep)
     assert not bad.any(), (name, rep, np.argwhere(bad)[:5])
     return rep
+
+
+def mfma_window_bound_rows(Ar, fa, Br, fb, t):
+    """hw for sampled outputs (i_n, j_n): Ar = A[ii], Br = B[jj] (rows of the
+    sampled outputs only), t a scalar (tensorwise) or (sA[ii], sB[jj]) per-row
+    factors of every 128-long contraction block."""
+    ga, gb = group_max(Ar, fa), group_max(Br, fb)
+    c = 7 * 2.0 ** -12
+    if not isinstance(t, tuple):
+        return c * abs(float(t)) * (ga * gb).sum(axis=1)
+    sA, sB = (np.abs(np.asarray(x, np.float64)) for x in t)
+    out = 0.0
+    for kb in range(sA.shape[1]):
+        g = slice(16 * kb, 16 * kb + 16)
+        out = out + (ga[:, g] * gb[:, g]).sum(axis=1) * sA[:, kb] * sB[:, kb]
+    return c * out
