@@ -49,12 +49,10 @@ namespace fp8k {
 constexpr int kThreads = 256;
 
 // Tile configuration: BM x BN output tile, BK contraction step, S LDS stages,
-// WNJ 32-column blocks per wave (wave tile 128 x 32*WNJ), OCC workgroups per
-// CU, EPI = 1 stages the bf16 epilogue through a per-wave LDS slice (32 rows
-// at a time) so every store instruction writes whole row segments.
-template <int BM_, int BN_, int BK_, int S_, int WNJ_, int OCC_, int EPI_ = 0>
+// WNJ 32-column blocks per wave (wave tile 128 x 32*WNJ), OCC workgroups per CU.
+template <int BM_, int BN_, int BK_, int S_, int WNJ_, int OCC_>
 struct GemmCfg {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WNJ = WNJ_, OCC = OCC_, EPI = EPI_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_, WNJ = WNJ_, OCC = OCC_;
     static_assert(BM == 256 && BN == 2 * WNJ * 32, "4 waves in 2 x 2, wave tile 128 x 32*WNJ");
     static_assert(BK == 64 || BK == 128, "BK");
 };
@@ -72,15 +70,6 @@ struct GemmArgs {
     int ktiles;       // K / BK
     int items;        // tiles_i * tiles_j * splits
 };
-
-// 32 bytes of LDS row `row` (logical 16-byte chunks c0, c0 + 1)
-template <int BK>
-__device__ __forceinline__ v8i lds_frag(const uint8_t* tile, int row, int c0) {
-    const int s = swz<BK>(row);
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * BK + ((c0 ^ s) << 4));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + row * BK + (((c0 + 1) ^ s) << 4));
-    return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
 
 struct Item {
     int ti, tj, z, kb, ke;
@@ -122,14 +111,13 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_kernel(GemmArgs g) {
     constexpr int L = LA + LB + (BLOCK ? 2 : 0);   // LDS-DMA instructions per wave per stage
     constexpr int RPK = 1024 / BK;   // rows per 1 KiB LDS block
     constexpr int CPR = BK / 16;     // 16-byte chunks per row
-    constexpr int ECH = WNJ * 4;     // 16-byte chunks per epilogue row (32*WNJ bf16)
-    constexpr int EPI_BYTES = C::EPI ? 4 * 32 * ECH * 16 : 0;   // four per-wave slices
-    static_assert(S * STAGE + EPI_BYTES <= 160 * 1024, "LDS");
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE + EPI_BYTES];
+    static_assert(S * STAGE <= 160 * 1024, "LDS");
+    static_assert(BLOCK && BK == 128 && WNJ == 2, "block-scaled kernel: BK 128, wave tile 128 x 64");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wi = wave >> 1, wj = wave & 1;
 
     // ---- load cursor (runs S-1 stages ahead of the compute cursor) -------
@@ -239,9 +227,13 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_kernel(GemmArgs g) {
     const int frow = lane & 31;                    // fragment row within a 32-row block
     const int arow = wi * 128 + frow;
     const int brow = wj * (WNJ * 32) + frow;
-    const bool sb_per_row = BLOCK && g.sb.group == 1;
-    float t_tensor = 1.0f;
-    if constexpr (!BLOCK) t_tensor = g.sa.sinv[0] * g.sb.sinv[0];
+    const bool sb_per_row = g.sb.group == 1;
+    const int ch = (lane >> 5) * 2;
+    const uint32_t smem0 = lds_off(smem);
+    // fragment rows in a stage: chunk ch (ch+1 at ^16; the second 64-long half
+    // at ^64), +4096 bytes per 32-row block
+    const uint32_t offA = (uint32_t)(arow * BK + ((ch ^ swz<BK>(arow)) << 4));
+    const uint32_t offB = (uint32_t)(A_BYTES + brow * BK + ((ch ^ swz<BK>(brow)) << 4));
 
 #define FP8K_STEP(FIRST)                                                                   \
     do {                                                                                   \
@@ -272,103 +264,99 @@ __global__ __launch_bounds__(kThreads, C::OCC) void gemm_kernel(GemmArgs g) {
         barrier_lds(); \
         if (l_ok) FP8K_ISSUE_STAGE(); \
  \
-        const uint8_t* sA = smem + (consumed % S) * STAGE; \
-        const uint8_t* sB = sA + A_BYTES; \
-        if constexpr (!BLOCK) { \
-            /* BK/64 matrix-core steps; the fragments of step kk+1 are read \
-               from LDS before the MFMAs of step kk are issued */ \
-            constexpr int KK = BK / 64; \
-            v8i af[2][4], bf[2][WNJ]; \
-_Pragma("unroll") \
-            for (int mi = 0; mi < 4; mi++) af[0][mi] = lds_frag<BK>(sA, arow + mi * 32, (lane >> 5) * 2); \
-_Pragma("unroll") \
-            for (int nj = 0; nj < WNJ; nj++) bf[0][nj] = lds_frag<BK>(sB, brow + nj * 32, (lane >> 5) * 2); \
-_Pragma("unroll") \
-            for (int kk = 0; kk < KK; kk++) { \
-                if (kk + 1 < KK) { \
-_Pragma("unroll") \
-                    for (int mi = 0; mi < 4; mi++) \
-                        af[(kk + 1) & 1][mi] = lds_frag<BK>(sA, arow + mi * 32, 4 * (kk + 1) + (lane >> 5) * 2); \
-_Pragma("unroll") \
-                    for (int nj = 0; nj < WNJ; nj++) \
-                        bf[(kk + 1) & 1][nj] = lds_frag<BK>(sB, brow + nj * 32, 4 * (kk + 1) + (lane >> 5) * 2); \
-                } \
-_Pragma("unroll") \
-                for (int mi = 0; mi < 4; mi++) \
-_Pragma("unroll") \
-                    for (int nj = 0; nj < WNJ; nj++) \
-                        acc[mi][nj] = mfma<FA, FB>(bf[kk & 1][nj], af[kk & 1][mi], \
-                                                   (FIRST && kk == 0) ? vzero : acc[mi][nj]); \
-            } \
-        } else { \
- /* fp32 factors of this 128-long contraction block (staged in LDS); */ \
- /* rows past I or J hold the factor of row I-1 / J-1 */ \
-            const float* sAs = reinterpret_cast<const float*>(sA + A_BYTES + B_BYTES); \
-            const float* sBs = sAs + BM; \
-            float sa_v[4]; \
-_Pragma("unroll") \
-            for (int mi = 0; mi < 4; mi++) sa_v[mi] = sAs[arow + mi * 32]; \
-            float sb_v[WNJ][16]; \
-            float sb_u = 0.0f; \
+        /* LDS reads in inline assembly (no compiler vmcnt(0) in front of
+           them), each group issued and waited for inside one asm statement:
+           the stage's fp32 factors, then the fragments of each 64-long half
+           of the 128-block */ \
+        const uint32_t sb_ = smem0 + (uint32_t)((consumed % S) * STAGE); \
+        float sa_v[4]; \
+        float sb_v[WNJ][16]; \
+        float sb_u = 0.0f; \
+        { \
+            const uint32_t sc_ = sb_ + A_BYTES + B_BYTES; \
+            const uint32_t pa_ = sc_ + (uint32_t)(arow * 4); \
             if (sb_per_row) { \
-                const int jb = wj * (WNJ * 32) + 4 * (lane >> 5); \
+                const uint32_t pb_ = sc_ + (uint32_t)(BM * 4 + (wj * (WNJ * 32) + 4 * (lane >> 5)) * 4); \
+                f32x4 g0_, g1_, g2_, g3_, g4_, g5_, g6_, g7_; \
+                asm volatile("ds_read_b32 %0, %12 offset:0\n\t" \
+                             "ds_read_b32 %1, %12 offset:128\n\t" \
+                             "ds_read_b32 %2, %12 offset:256\n\t" \
+                             "ds_read_b32 %3, %12 offset:384\n\t" \
+                             "ds_read_b128 %4, %13 offset:0\n\t" \
+                             "ds_read_b128 %5, %13 offset:32\n\t" \
+                             "ds_read_b128 %6, %13 offset:64\n\t" \
+                             "ds_read_b128 %7, %13 offset:96\n\t" \
+                             "ds_read_b128 %8, %13 offset:128\n\t" \
+                             "ds_read_b128 %9, %13 offset:160\n\t" \
+                             "ds_read_b128 %10, %13 offset:192\n\t" \
+                             "ds_read_b128 %11, %13 offset:224\n\t" \
+                             "s_waitcnt lgkmcnt(0)" \
+                             : "=&v"(sa_v[0]), "=&v"(sa_v[1]), "=&v"(sa_v[2]), "=&v"(sa_v[3]), \
+                               "=&v"(g0_), "=&v"(g1_), "=&v"(g2_), "=&v"(g3_), \
+                               "=&v"(g4_), "=&v"(g5_), "=&v"(g6_), "=&v"(g7_) \
+                             : "v"(pa_), "v"(pb_) \
+                             : "memory"); \
+                /* element e of float4 q of column block nj: column 8q + e (+4 for lanes 32..63) */ \
+                const f32x4 gq_[WNJ][4] = {{g0_, g1_, g2_, g3_}, {g4_, g5_, g6_, g7_}}; \
 _Pragma("unroll") \
                 for (int nj = 0; nj < WNJ; nj++) \
 _Pragma("unroll") \
                     for (int q = 0; q < 4; q++) { \
-                        const float4 f = *reinterpret_cast<const float4*>(sBs + jb + nj * 32 + 8 * q); \
-                        sb_v[nj][4 * q] = f.x; \
-                        sb_v[nj][4 * q + 1] = f.y; \
-                        sb_v[nj][4 * q + 2] = f.z; \
-                        sb_v[nj][4 * q + 3] = f.w; \
+                        sb_v[nj][4 * q + 0] = gq_[nj][q].x; \
+                        sb_v[nj][4 * q + 1] = gq_[nj][q].y; \
+                        sb_v[nj][4 * q + 2] = gq_[nj][q].z; \
+                        sb_v[nj][4 * q + 3] = gq_[nj][q].w; \
                     } \
             } else { \
-                sb_u = sBs[wj * (WNJ * 32)]; \
+                const uint32_t pb_ = sc_ + (uint32_t)(BM * 4 + wj * (WNJ * 32) * 4); \
+                asm volatile("ds_read_b32 %0, %5 offset:0\n\t" \
+                             "ds_read_b32 %1, %5 offset:128\n\t" \
+                             "ds_read_b32 %2, %5 offset:256\n\t" \
+                             "ds_read_b32 %3, %5 offset:384\n\t" \
+                             "ds_read_b32 %4, %6\n\t" \
+                             "s_waitcnt lgkmcnt(0)" \
+                             : "=&v"(sa_v[0]), "=&v"(sa_v[1]), "=&v"(sa_v[2]), "=&v"(sa_v[3]), "=&v"(sb_u) \
+                             : "v"(pa_), "v"(pb_) \
+                             : "memory"); \
             } \
-            v16f p[4][WNJ]; \
-            { \
-                v8i af[4], bf[WNJ]; \
-_Pragma("unroll") \
-                for (int mi = 0; mi < 4; mi++) af[mi] = lds_frag<BK>(sA, arow + mi * 32, (lane >> 5) * 2); \
-_Pragma("unroll") \
-                for (int nj = 0; nj < WNJ; nj++) bf[nj] = lds_frag<BK>(sB, brow + nj * 32, (lane >> 5) * 2); \
-                const v16f zero = {}; \
-_Pragma("unroll") \
-                for (int mi = 0; mi < 4; mi++) \
-_Pragma("unroll") \
-                    for (int nj = 0; nj < WNJ; nj++) p[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], zero); \
-            } \
-            { \
-                v8i af[4], bf[WNJ]; \
-_Pragma("unroll") \
-                for (int mi = 0; mi < 4; mi++) af[mi] = lds_frag<BK>(sA, arow + mi * 32, 4 + (lane >> 5) * 2); \
-_Pragma("unroll") \
-                for (int nj = 0; nj < WNJ; nj++) bf[nj] = lds_frag<BK>(sB, brow + nj * 32, 4 + (lane >> 5) * 2); \
-_Pragma("unroll") \
-                for (int mi = 0; mi < 4; mi++) \
-_Pragma("unroll") \
-                    for (int nj = 0; nj < WNJ; nj++) p[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], p[mi][nj]); \
-            } \
+        } \
+        const uint32_t a0_ = sb_ + offA, a1_ = a0_ ^ 16u, b0_ = sb_ + offB, b1_ = b0_ ^ 16u; \
+        v16f p[4][WNJ]; \
+        { \
+            v8i af[4], bf[WNJ]; \
+            ds_frags6_wait(af, bf, a0_, a1_, b0_, b1_); \
+            const v16f zero = {}; \
 _Pragma("unroll") \
             for (int mi = 0; mi < 4; mi++) \
 _Pragma("unroll") \
-                for (int nj = 0; nj < WNJ; nj++) { \
-                    if (sb_per_row) { \
-_Pragma("unroll") \
-                        for (int v = 0; v < 16; v++) \
-                            acc[mi][nj][v] = FIRST ? p[mi][nj][v] * (sa_v[mi] * sb_v[nj][v]) : __builtin_fmaf(p[mi][nj][v], sa_v[mi] * sb_v[nj][v], acc[mi][nj][v]); \
-                    } else { \
-                        const float t = sa_v[mi] * sb_u; \
-_Pragma("unroll") \
-                        for (int v = 0; v < 16; v++) acc[mi][nj][v] = FIRST ? p[mi][nj][v] * t : __builtin_fmaf(p[mi][nj][v], t, acc[mi][nj][v]); \
-                    } \
-                } \
+                for (int nj = 0; nj < WNJ; nj++) p[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], zero); \
         } \
+        { \
+            /* second half of the block: chunks 4..7 of the same rows */ \
+            v8i af[4], bf[WNJ]; \
+            ds_frags6_wait(af, bf, a0_ ^ 64u, a1_ ^ 64u, b0_ ^ 64u, b1_ ^ 64u); \
+_Pragma("unroll") \
+            for (int mi = 0; mi < 4; mi++) \
+_Pragma("unroll") \
+                for (int nj = 0; nj < WNJ; nj++) p[mi][nj] = mfma<FA, FB>(bf[nj], af[mi], p[mi][nj]); \
+        } \
+_Pragma("unroll") \
+        for (int mi = 0; mi < 4; mi++) \
+_Pragma("unroll") \
+            for (int nj = 0; nj < WNJ; nj++) { \
+                if (sb_per_row) { \
+_Pragma("unroll") \
+                    for (int v = 0; v < 16; v++) \
+                        acc[mi][nj][v] = FIRST ? p[mi][nj][v] * (sa_v[mi] * sb_v[nj][v]) : __builtin_fmaf(p[mi][nj][v], sa_v[mi] * sb_v[nj][v], acc[mi][nj][v]); \
+                } else { \
+                    const float t = sa_v[mi] * sb_u; \
+_Pragma("unroll") \
+                    for (int v = 0; v < 16; v++) acc[mi][nj][v] = FIRST ? p[mi][nj][v] * t : __builtin_fmaf(p[mi][nj][v], t, acc[mi][nj][v]); \
+                } \
+            } \
         consumed++;                                                                        \
     } while (0)
 
-    const v16f vzero = {};
-    (void)vzero;
     while (true) {
         FP8K_STEP(true);
         for (int kt = c_it.kb + 1; kt < c_it.ke; kt++) {
@@ -385,7 +373,7 @@ _Pragma("unroll") \
             const bool i_ok0 = i0 + wi * 128 < g.I;                   // mi blocks share it
             const int nj_ok = jw >= g.J ? 0 : WNJ;                    // wave's columns all valid or none
             // the wave issues all of the stores below or none of them
-            if (i_ok0 && nj_ok) ops += (C::EPI && g.splits == 1) ? 4 * (32 * ECH / 64) : 4 * WNJ * 4;
+            if (i_ok0 && nj_ok) ops += 4 * WNJ * 4;
             if (g.splits > 1) {
                 float* out = g.part + (int64_t)c_it.z * g.I * g.J + my_i * g.J + my_j;
                 if (i_ok0 && nj_ok) {
@@ -399,43 +387,8 @@ _Pragma("unroll") \
                                     make_float4(acc[mi][nj][4 * q], acc[mi][nj][4 * q + 1], acc[mi][nj][4 * q + 2],
                                                 acc[mi][nj][4 * q + 3]);
                 }
-            } else if constexpr (C::EPI) {
-                // per-wave slice: 32 rows x ECH chunks, chunk c of row r stored at c ^ (r % ECH)
-                const float t = BLOCK ? 1.0f : t_tensor;
-                uint8_t* slice = smem + S * STAGE + wave * (32 * ECH * 16);
-                // row-major read-back: lane covers chunk (idx % ECH) of row (idx / ECH)
-                uint16_t* out_base = g.c + (i0 + wi * 128) * g.J + jw;
-                if (i_ok0 && nj_ok) {
-#pragma unroll
-                    for (int mi = 0; mi < 4; mi++) {
-#pragma unroll
-                        for (int nj = 0; nj < WNJ; nj++)
-#pragma unroll
-                            for (int q = 0; q < 4; q++) {
-                                const __bf16 h0 = (__bf16)(acc[mi][nj][4 * q] * t);
-                                const __bf16 h1 = (__bf16)(acc[mi][nj][4 * q + 1] * t);
-                                const __bf16 h2 = (__bf16)(acc[mi][nj][4 * q + 2] * t);
-                                const __bf16 h3 = (__bf16)(acc[mi][nj][4 * q + 3] * t);
-                                uint2 w;
-                                w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-                                      ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                                w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) |
-                                      ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                                const int chunk = nj * 4 + q;
-                                *reinterpret_cast<uint2*>(slice + frow * (ECH * 16) + ((chunk ^ (frow % ECH)) << 4) +
-                                                          (lane >> 5) * 8) = w;
-                            }
-#pragma unroll
-                        for (int p = 0; p < 32 * ECH / 64; p++) {
-                            const int idx = p * 64 + lane;
-                            const int r = idx / ECH, c = idx % ECH;
-                            const uint4 w = *reinterpret_cast<const uint4*>(slice + r * (ECH * 16) + ((c ^ (r % ECH)) << 4));
-                            *reinterpret_cast<uint4*>(out_base + (int64_t)(mi * 32 + r) * g.J + c * 8) = w;
-                        }
-                    }
-                }
             } else {
-                const float t = BLOCK ? 1.0f : t_tensor;
+                // block-scaled: the factors are already in the accumulators
                 uint16_t* out = g.c + my_i * g.J + my_j;
                 if (i_ok0 && nj_ok) {
 #pragma unroll
@@ -444,10 +397,10 @@ _Pragma("unroll") \
                         for (int nj = 0; nj < WNJ; nj++)
 #pragma unroll
                             for (int q = 0; q < 4; q++) {
-                                const __bf16 h0 = (__bf16)(acc[mi][nj][4 * q] * t);
-                                const __bf16 h1 = (__bf16)(acc[mi][nj][4 * q + 1] * t);
-                                const __bf16 h2 = (__bf16)(acc[mi][nj][4 * q + 2] * t);
-                                const __bf16 h3 = (__bf16)(acc[mi][nj][4 * q + 3] * t);
+                                const __bf16 h0 = (__bf16)acc[mi][nj][4 * q];
+                                const __bf16 h1 = (__bf16)acc[mi][nj][4 * q + 1];
+                                const __bf16 h2 = (__bf16)acc[mi][nj][4 * q + 2];
+                                const __bf16 h3 = (__bf16)acc[mi][nj][4 * q + 3];
                                 uint2 w;
                                 w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
                                       ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);

@@ -26,7 +26,9 @@
 //  - the hand-off of a stage is one s_waitcnt vmcnt(n) on the wave's own DMA
 //    (n counted exactly: the loads and epilogue stores issued after it) plus
 //    the barrier; fragment reads are inline assembly so the compiler adds no
-//    vmcnt(0) in front of them.
+//    vmcnt(0) in front of them.  Their destination registers stay live
+//    operands of an lgkmcnt(0) wait (the next barrier, or the wait before the
+//    final epilogue), so no register with a load in flight is reused.
 //  - epilogue: each wave converts 32 rows at a time to bf16 into a private
 //    4 KiB LDS slice (chunk-major, (row ^ 2 chunk) swizzle: conflict-free
 //    writes and reads) and stores whole 128-byte row segments.
@@ -326,6 +328,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     }
 #undef FP8K_STEP
 #undef FP8K_MF
+    // The last step's fragment reads (of a re-read stage) are dead but still
+    // in flight: let them land before the epilogue's temporaries can reuse
+    // their registers.
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb0[0]), "+v"(fb0[1]), "+v"(fb1[0]),
+                   "+v"(fb1[1])
+                 :
+                 : "memory");
     if (have_prev) epilogue(p_it);
     wait_vm<0>();
 }
