@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-stage breakdown")
+    ap.add_argument("--no-block", action="store_true", help="skip the block-scaling run")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after the steps, negate a 512 MiB fp16 tensor (counter calibration)")
     ap.add_argument("--summarize", metavar="PREFIX", help="summarize PREFIX_kernel_trace.csv / "
@@ -229,23 +230,39 @@ def summarize(prefix, steps, warmup):
     print("\n".join(out))
 
 
-def stage_times(fp8, torch, layers, reps):
+def stage_times(fp8, torch, layers, reps, recipe="tensor"):
     """Average duration of each kernel-level call of one step, timed with
     events on the stream the kernels run on (torch's current stream)."""
     res = []
+    E4, E5 = fp8.E4M3, fp8.E5M2
+    block = recipe == "block"
+    act = fp8.SCALE_1x128 if block else fp8.SCALE_TENSOR
+    wsc = fp8.SCALE_128x128 if block else fp8.SCALE_TENSOR
+    # algorithmic bytes per element: tensorwise = amax read 2 + cast read 2 +
+    # two 1-byte layouts; block = one read + two layouts + fp32 scale and
+    # inverse scale per 128-block of each layout (1x128) or per tile (128x128)
+    act_b, w_b = (4 + 16 / 128, 4 + 8 / 16384) if block else (6, 6)
     for L in layers:
         lin, N, K, M = L["lin"], L["N"], L["K"], L["M"]
         wq = lin.w_q
-        E4, E5, T = fp8.E4M3, fp8.E5M2, fp8.SCALE_TENSOR
-        sx, sw, sdy = (fp8.gemm_scale(t.scale_inv) for t in (lin.saved_x, wq, lin.dy_q))
+        if block:
+            sx = fp8.gemm_scale(lin.saved_x.scale_inv, 1, K // 128, 1)
+            sw = fp8.gemm_scale(wq.scale_inv, 128, K // 128, 1)
+            sdy = fp8.gemm_scale(lin.dy_q.scale_inv, 1, M // 128, 1)
+            swt = fp8.gemm_scale(wq.scale_inv, 128, 1, K // 128)
+            sdyc = fp8.gemm_scale(lin.dy_q.scale_inv_col, 1, N // 128, 1)
+            sxc = fp8.gemm_scale(lin.saved_x.scale_inv_col, 1, N // 128, 1)
+        else:
+            sx, sw, sdy = (fp8.gemm_scale(t.scale_inv) for t in (lin.saved_x, wq, lin.dy_q))
+            swt, sdyc, sxc = sw, sdy, sx
         tag = "%dx%d" % (K, M)
         calls = [
-            ("quant_x_" + tag, "quant", N * K, lambda: fp8.quantize(L["x"], E4, T, out=lin.saved_x)),
-            ("quant_w_" + tag, "quant", M * K, lambda: fp8.quantize(L["w"], E4, T, out=wq)),
+            ("quant_x_" + tag, "quant", N * K * act_b, lambda: fp8.quantize(L["x"], E4, act, out=lin.saved_x)),
+            ("quant_w_" + tag, "quant", M * K * w_b, lambda: fp8.quantize(L["w"], E4, wsc, out=wq)),
             ("gemm_fprop_" + tag, "gemm", (N, M, K), lambda: fp8.gemm(lin.saved_x.q_row, E4, sx, wq.q_row, E4, sw, out=L["y"])),
-            ("quant_dy_" + tag, "quant", N * M, lambda: fp8.quantize(L["dy"], E5, T, out=lin.dy_q)),
-            ("gemm_dgrad_" + tag, "gemm", (N, K, M), lambda: fp8.gemm(lin.dy_q.q_row, E5, sdy, wq.q_col, E4, sw, out=L["dx"])),
-            ("gemm_wgrad_" + tag, "gemm", (M, K, N), lambda: fp8.gemm(lin.dy_q.q_col, E5, sdy, lin.saved_x.q_col, E4, sx, out=L["dw"])),
+            ("quant_dy_" + tag, "quant", N * M * act_b, lambda: fp8.quantize(L["dy"], E5, act, out=lin.dy_q)),
+            ("gemm_dgrad_" + tag, "gemm", (N, K, M), lambda: fp8.gemm(lin.dy_q.q_row, E5, sdy, wq.q_col, E4, swt, out=L["dx"])),
+            ("gemm_wgrad_" + tag, "gemm", (M, K, N), lambda: fp8.gemm(lin.dy_q.q_col, E5, sdyc, lin.saved_x.q_col, E4, sxc, out=L["dw"])),
         ]
         for name, kind, size, fn in calls:
             for _ in range(3):
@@ -259,7 +276,7 @@ def stage_times(fp8, torch, layers, reps):
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
             if kind == "quant":
-                byts = 6 * size            # amax read 2 + cast read 2 + two 1-byte layouts
+                byts = int(size)
                 res.append({"stage": name, "ms": ms, "bytes": byts, "gbs": byts / ms / 1e6})
             else:
                 I, J, Kc = size
@@ -268,6 +285,37 @@ def stage_times(fp8, torch, layers, reps):
                 res.append({"stage": name, "ms": ms, "flops": flops, "bytes": byts,
                             "tflops": flops / ms / 1e9, "gbs": byts / ms / 1e6, "ai": flops / byts})
     return res
+
+
+def make_layers(fp8, torch, synth, N, recipe, dev):
+    R = fp8.RECIPE_BLOCK if recipe == "block" else fp8.RECIPE_TENSOR
+    layers = []
+    for idx, (K, M) in enumerate(SHAPES):
+        x, w, dy = synth.operands_on_device(N, K, M, seed=idx, device=dev)
+        layers.append({"N": N, "K": K, "M": M, "x": x, "w": w, "dy": dy, "lin": fp8.Fp8Linear(N, K, M, R, device=dev),
+                       "y": torch.empty((N, M), dtype=torch.bfloat16, device=dev),
+                       "dx": torch.empty((N, K), dtype=torch.bfloat16, device=dev),
+                       "dw": torch.empty((M, K), dtype=torch.bfloat16, device=dev)})
+    return layers
+
+
+def time_steps(torch, layers, steps, warmup):
+    """ms per step (events around `steps` steps after `warmup` untimed ones)."""
+    def step():
+        for L in layers:
+            L["lin"].forward(L["x"], L["w"], y=L["y"])
+            L["lin"].backward(L["dy"], dx=L["dx"], dw=L["dw"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def measured_traffic(stage):
@@ -340,32 +388,10 @@ def main():
     torch.cuda.set_device(dev)
     N = args.tokens
     shapes = SHAPES
-    layers = []
-    for idx, (K, M) in enumerate(shapes):
-        x, w, dy = synth.operands_on_device(N, K, M, seed=idx, device=dev)
-        lin = fp8.Fp8Linear(N, K, M, fp8.RECIPE_TENSOR, device=dev)
-        layers.append({"N": N, "K": K, "M": M, "x": x, "w": w, "dy": dy, "lin": lin,
-                       "y": torch.empty((N, M), dtype=torch.bfloat16, device=dev),
-                       "dx": torch.empty((N, K), dtype=torch.bfloat16, device=dev),
-                       "dw": torch.empty((M, K), dtype=torch.bfloat16, device=dev)})
-
-    def step():
-        for L in layers:
-            L["lin"].forward(L["x"], L["w"], y=L["y"])
-            L["lin"].backward(L["dy"], dx=L["dx"], dw=L["dw"])
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    layers = make_layers(fp8, torch, synth, N, "tensor", dev)
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
+    ms = time_steps(torch, layers, args.steps, args.warmup)
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
     flops = sum(6 * N * K * M for K, M in shapes)
     value = flops / (ms / 1e3) / 1e12
     print("timed %d steps: %.4f ms/step (wall %.3f s)" % (args.steps, ms, wall), file=sys.stderr, flush=True)
@@ -387,6 +413,26 @@ def main():
     q = [s for s in stages if s["stage"].startswith("quant")]
     quant_gbs = sum(s["bytes"] for s in q) / sum(s["ms"] for s in q) / 1e6
     dom = max(stages, key=lambda s: s["ms"])     # the stage (one library call) that takes longest
+    block = None
+    if not args.no_block:
+        # the same two linears under block scaling (X, dY 1x128; W 128x128)
+        del layers
+        torch.cuda.empty_cache()
+        blayers = make_layers(fp8, torch, synth, N, "block", dev)
+        bms = time_steps(torch, blayers, args.steps, args.warmup)
+        bst = stage_times(fp8, torch, blayers, args.reps, "block")
+        print("block scaling: %.4f ms/step" % bms, file=sys.stderr, flush=True)
+        for st in bst:
+            print("  %-24s %8.4f ms  %s" % (st["stage"], st["ms"],
+                                            ("%.1f TFLOP/s %.0f GB/s" % (st["tflops"], st["gbs"])) if "flops" in st
+                                            else "%.0f GB/s" % st["gbs"]), file=sys.stderr, flush=True)
+        bq = [st for st in bst if st["stage"].startswith("quant")]
+        block = {"recipe": "X, dY 1x128 blocks; W 128x128 blocks", "value": round(flops / (bms / 1e3) / 1e12, 2),
+                 "unit": "TFLOP/s", "ms_per_step": round(bms, 4),
+                 "quantize_gbs": round(sum(st["bytes"] for st in bq) / sum(st["ms"] for st in bq) / 1e6, 1),
+                 "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in st.items()} for st in bst],
+                 "roofline": roofline_of(max(bst, key=lambda st: st["ms"]))}
+        block["roofline"]["traffic"] = None
     pages_tflops = sum(6 * 131072 * K * M for K, M in shapes) / (sum(PAGES_MS[s] for s in shapes) / 1e3) / 1e12
 
     out = {
@@ -402,6 +448,7 @@ def main():
         "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in stages],
         "roofline": roofline_of(dom),
         "cpu_baseline": None,
+        "block_scaling": block,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens)

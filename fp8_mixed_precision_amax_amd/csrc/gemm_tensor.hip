@@ -10,7 +10,7 @@
 // Design
 //  - persistent: one workgroup per CU walks work items (256 x 256 output
 //    tile, split-K slice) dealt XCD by XCD (the dispatcher puts workgroup b on
-//    XCD b % 8) and rastered in groups of 8 tile rows, so the workgroups of one
+//    XCD b % 8) and rastered in groups of 2 tile rows, so the workgroups of one
 //    XCD share A and B tiles through its L2.
 //  - 8 waves, two per SIMD, wave tile 128 x 64 (4 x 2 blocks of
 //    v_mfma_f32_32x32x64_f8f6f4, 128 accumulator registers), all waves in
@@ -74,7 +74,10 @@ __device__ __forceinline__ bool item_at(const Args& g, int r, Item& it) {
     if (Lg >= g.items) return false;
     const int tiles = g.tiles_i * g.tiles_j;
     const int z = Lg / tiles, t = Lg - z * tiles;
-    constexpr int GI = 8;
+    // groups of 2 tile rows: the workgroups of an XCD share B tiles across
+    // the group and A tiles along it; measured best of 2..32 on the K = 512
+    // output-heavy shapes (-8 %) and equal elsewhere
+    constexpr int GI = 2;
     const int per_group = GI * g.tiles_j, grp = t / per_group, local = t - grp * per_group;
     int rows = g.tiles_i - grp * GI;
     rows = rows < GI ? rows : GI;
