@@ -246,12 +246,12 @@ def stage_times(fp8, torch, layers, reps, recipe="tensor"):
         lin, N, K, M = L["lin"], L["N"], L["K"], L["M"]
         wq = lin.w_q
         if block:
-            sx = fp8.gemm_scale(lin.saved_x.scale_inv, 1, K // 128, 1)
-            sw = fp8.gemm_scale(wq.scale_inv, 128, K // 128, 1)
-            sdy = fp8.gemm_scale(lin.dy_q.scale_inv, 1, M // 128, 1)
-            swt = fp8.gemm_scale(wq.scale_inv, 128, 1, K // 128)
-            sdyc = fp8.gemm_scale(lin.dy_q.scale_inv_col, 1, N // 128, 1)
-            sxc = fp8.gemm_scale(lin.saved_x.scale_inv_col, 1, N // 128, 1)
+            sx = fp8.block_gemm_scale(lin.saved_x.scale_inv, 1)
+            sw = fp8.block_gemm_scale(wq.scale_inv, 128)
+            sdy = fp8.block_gemm_scale(lin.dy_q.scale_inv, 1)
+            swt = fp8.block_gemm_scale(wq.scale_inv.t(), 128)
+            sdyc = fp8.block_gemm_scale(lin.dy_q.scale_inv_col, 1)
+            sxc = fp8.block_gemm_scale(lin.saved_x.scale_inv_col, 1)
         else:
             sx, sw, sdy = (fp8.gemm_scale(t.scale_inv) for t in (lin.saved_x, wq, lin.dy_q))
             swt, sdyc, sxc = sw, sdy, sx

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import (E4M3, E5M2, LAYOUT_COL, LAYOUT_ROW, RECIPE_BLOCK, RECIPE_TENSOR, SCALE_1x128,
                    SCALE_128x128, SCALE_TENSOR, Fp8Error)
 
-__all__ = ["E4M3", "E5M2", "SCALE_TENSOR", "SCALE_1x128", "SCALE_128x128", "RECIPE_TENSOR",
+__all__ = ["block_gemm_scale", "E4M3", "E5M2", "SCALE_TENSOR", "SCALE_1x128", "SCALE_128x128", "RECIPE_TENSOR",
            "RECIPE_BLOCK", "LAYOUT_ROW", "LAYOUT_COL", "Fp8Error", "QTensor", "quantize",
            "gemm", "WeightCache", "Fp8Linear", "linear_workspace", "lib"]
 
@@ -49,17 +49,24 @@ class QTensor:
         u8, f32 = torch.uint8, torch.float32
         self.q_row = torch.empty((rows, cols), dtype=u8, device=device) if row else None
         self.q_col = torch.empty((cols, rows), dtype=u8, device=device) if col else None
+        # 1x128 scales are stored block-major ([cols/128, rows] and
+        # [rows/128, cols]); the attributes are transposed views with the
+        # logical shapes [rows, cols/128] and [cols, rows/128]
         if scaling == SCALE_TENSOR:
             shp = (1,)
         elif scaling == SCALE_1x128:
             shp = (rows, cols // 128)
         else:
             shp = (rows // 128, cols // 128)
-        self.scale = torch.empty(shp, dtype=f32, device=device)
-        self.scale_inv = torch.empty(shp, dtype=f32, device=device)
+        if scaling == SCALE_1x128:
+            self.scale = torch.empty((cols // 128, rows), dtype=f32, device=device).t()
+            self.scale_inv = torch.empty((cols // 128, rows), dtype=f32, device=device).t()
+        else:
+            self.scale = torch.empty(shp, dtype=f32, device=device)
+            self.scale_inv = torch.empty(shp, dtype=f32, device=device)
         if scaling == SCALE_1x128 and col:
-            self.scale_col = torch.empty((cols, rows // 128), dtype=f32, device=device)
-            self.scale_inv_col = torch.empty((cols, rows // 128), dtype=f32, device=device)
+            self.scale_col = torch.empty((rows // 128, cols), dtype=f32, device=device).t()
+            self.scale_inv_col = torch.empty((rows // 128, cols), dtype=f32, device=device).t()
         else:
             self.scale_col = self.scale_inv_col = None
         self.amax = torch.empty((1,), dtype=f32, device=device) if scaling == SCALE_TENSOR else None
@@ -93,6 +100,13 @@ def gemm_scale(sinv, group=0, stride_r=0, stride_kb=0):
     s = _lib.GemmScaleC(sinv.data_ptr(), group, stride_r, stride_kb)
     s._keep = sinv
     return s
+
+
+def block_gemm_scale(sinv, group):
+    """Scale descriptor of a block-scaled operand whose factors are the 2-D
+    tensor sinv [operand rows / group, contraction blocks] (any strides, e.g.
+    the views a QTensor holds)."""
+    return gemm_scale(sinv, group, sinv.stride(0), sinv.stride(1))
 
 
 def gemm(a, fa, sa, b, fb, sb, out=None, stream=None):

@@ -88,13 +88,15 @@ fp8_status check_quantize(const void* x, int64_t rows, int64_t cols, int format,
     if (layouts & FP8_LAYOUT_ROW) FP8_TRY(check_ptr16("q_row", out->q_row));
     if (layouts & FP8_LAYOUT_COL) FP8_TRY(check_ptr16("q_col", out->q_col));
     const bool row_scales = scaling != FP8_SCALE_BLOCK_1x128 || (layouts & FP8_LAYOUT_ROW);
+    // 1x128 scales are written as 8- and 16-byte runs: 16-byte alignment
+    auto check_scale = scaling == FP8_SCALE_BLOCK_1x128 ? check_ptr16 : check_ptr4;
     if (row_scales) {
-        FP8_TRY(check_ptr4("scale", out->scale));
-        FP8_TRY(check_ptr4("scale_inv", out->scale_inv));
+        FP8_TRY(check_scale("scale", out->scale));
+        FP8_TRY(check_scale("scale_inv", out->scale_inv));
     }
     if (scaling == FP8_SCALE_BLOCK_1x128 && (layouts & FP8_LAYOUT_COL)) {
-        FP8_TRY(check_ptr4("scale_col", out->scale_col));
-        FP8_TRY(check_ptr4("scale_inv_col", out->scale_inv_col));
+        FP8_TRY(check_scale("scale_col", out->scale_col));
+        FP8_TRY(check_scale("scale_inv_col", out->scale_inv_col));
     }
     if (out->amax && !aligned4(out->amax)) return fail(FP8_ERR_ALIGN, "amax is not 4-byte aligned");
     return FP8_OK;
@@ -322,7 +324,7 @@ fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, in
     if (recipe == FP8_RECIPE_TENSOR)
         return do_gemm(saved_x->q_row, FP8_E4M3, tensor_scale(saved_x->scale_inv), wq->q_row, FP8_E4M3,
                        tensor_scale(wq->scale_inv), N, M, K, y, gws, gws_bytes, st);
-    return do_gemm(saved_x->q_row, FP8_E4M3, block_scale(saved_x->scale_inv, 1, K / 128, 1), wq->q_row, FP8_E4M3,
+    return do_gemm(saved_x->q_row, FP8_E4M3, block_scale(saved_x->scale_inv, 1, 1, N), wq->q_row, FP8_E4M3,
                    block_scale(wq->scale_inv, 128, K / 128, 1), N, M, K, y, gws, gws_bytes, st);
 }
 
@@ -364,7 +366,7 @@ fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_r
             FP8_TRY(do_gemm(dy_q->q_row, FP8_E5M2, tensor_scale(dy_q->scale_inv), wq->q_col, FP8_E4M3,
                             tensor_scale(wq->scale_inv), N, K, M, dx, gws, gws_bytes, st));
         else
-            FP8_TRY(do_gemm(dy_q->q_row, FP8_E5M2, block_scale(dy_q->scale_inv, 1, M / 128, 1), wq->q_col, FP8_E4M3,
+            FP8_TRY(do_gemm(dy_q->q_row, FP8_E5M2, block_scale(dy_q->scale_inv, 1, 1, N), wq->q_col, FP8_E4M3,
                             block_scale(wq->scale_inv, 128, 1, K / 128), N, K, M, dx, gws, gws_bytes, st));
     }
     if (dw) {
@@ -372,8 +374,8 @@ fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_r
             FP8_TRY(do_gemm(dy_q->q_col, FP8_E5M2, tensor_scale(dy_q->scale_inv), saved_x->q_col, FP8_E4M3,
                             tensor_scale(saved_x->scale_inv), M, K, N, dw, gws, gws_bytes, st));
         else
-            FP8_TRY(do_gemm(dy_q->q_col, FP8_E5M2, block_scale(dy_q->scale_inv_col, 1, N / 128, 1), saved_x->q_col,
-                            FP8_E4M3, block_scale(saved_x->scale_inv_col, 1, N / 128, 1), M, K, N, dw, gws, gws_bytes,
+            FP8_TRY(do_gemm(dy_q->q_col, FP8_E5M2, block_scale(dy_q->scale_inv_col, 1, 1, M), saved_x->q_col,
+                            FP8_E4M3, block_scale(saved_x->scale_inv_col, 1, 1, K), M, K, N, dw, gws, gws_bytes,
                             st));
     }
     return FP8_OK;

@@ -67,9 +67,9 @@ struct CastArgs {
     int64_t R, C;
     uint8_t* q_row;     // [R, C] or null
     uint8_t* q_col;     // [C, R] or null
-    float* scale;       // tensor: [1]; 1x128: [R, C/128]; 128x128: [R/128, C/128]
+    float* scale;       // tensor: [1]; 1x128: [C/128, R] (block (r, cb) at cb*R + r); 128x128: [R/128, C/128]
     float* scale_inv;
-    float* scale_col;   // 1x128 only: [C, R/128]
+    float* scale_col;   // 1x128 only: [R/128, C] (block (c, rb) at rb*C + c)
     float* scale_inv_col;
     float* amax_out;    // tensor only, optional
     const uint16_t* partial;  // tensor only: kMaxAmaxPartials amax partials of pass 1 (unused slots 0)
@@ -170,7 +170,6 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
         }
     } else {
         // ---- MODE 1: 1x128 row blocks and 128x1 column blocks ------------
-        const int64_t cblocks = a.C >> 7, rblocks = a.R >> 7;
         if (a.q_row) {
             // row maxima: two rows per packed dword, reduced over the DPP row
             uint32_t rm[16];
@@ -181,21 +180,40 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
                 rm[p] = hmax_u16(m0) | (hmax_u16(m1) << 16);
                 rm[p] = row16_pkmax(rm[p]);
             }
+            // every lane of a 16-lane row group holds the maxima of the group's
+            // 32 rows; lane cb computes the scales of rows 2cb and 2cb+1 (the
+            // fp32 divisions once per row, not once per lane) and stores them:
+            // the tile's 128 row scales are one contiguous run of the
+            // block-column-major scale array
+            uint32_t mine = 0;
+#pragma unroll
+            for (int p = 0; p < 16; p++) mine = (p == cb) ? rm[p] : mine;
+            float s0, si0, s1, si1;
+            scale_from_amax_bits<FMT>(mine & 0xFFFFu, s0, si0);
+            scale_from_amax_bits<FMT>(mine >> 16, s1, si1);
+            {
+                const int64_t r0 = FP8K_ROW(2 * cb);   // rows 2cb, 2cb+1 are adjacent, r0 even
+                *reinterpret_cast<float2*>(a.scale + tc * a.R + r0) = make_float2(s0, s1);
+                *reinterpret_cast<float2*>(a.scale_inv + tc * a.R + r0) = make_float2(si0, si1);
+            }
+            // NaN patching only in tiles that hold a NaN (wave-uniform branch;
+            // patch_nan8 tests each element itself)
+            uint32_t mrow = rm[0];
+#pragma unroll
+            for (int p = 1; p < 16; p++) mrow = pkmax_u16(mrow, rm[p]);
+            const bool nan_rows = __ballot(hmax_u16(mrow) > 0x7F80u) != 0;
+            const int src0 = (lane & ~15) * 4;   // byte address of lane 0 of this row group
 #pragma unroll
             for (int p = 0; p < 16; p++) {
+                // scales of rows 2p, 2p+1 from lane p of the row group
+                const float sp0 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src0 + 4 * p, __builtin_bit_cast(int, s0)));
+                const float sp1 = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src0 + 4 * p, __builtin_bit_cast(int, s1)));
 #pragma unroll
                 for (int h = 0; h < 2; h++) {
                     const int i = 2 * p + h;
-                    const uint32_t m = h ? (rm[p] >> 16) : (rm[p] & 0xFFFFu);
-                    float s, si;
-                    scale_from_amax_bits<FMT>(m, s, si);
-                    uint2 c = enc8<FMT>(v[i], s);
-                    if (m > 0x7F80u) c = patch_nan8(v[i], c);
+                    uint2 c = enc8<FMT>(v[i], h ? sp1 : sp0);
+                    if (nan_rows) c = patch_nan8(v[i], c);
                     st_nt8(a.q_row + FP8K_ROW(i) * a.C + col0, c);
-                    if ((i >> 1) == cb) {   // lane cb writes the scales of its rows 2cb, 2cb+1
-                        a.scale[FP8K_ROW(i) * cblocks + tc] = s;
-                        a.scale_inv[FP8K_ROW(i) * cblocks + tc] = si;
-                    }
                 }
             }
         }
@@ -215,19 +233,24 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
                 cm[g] = pkmax_u16(cm[g], (uint32_t)__shfl_xor((int)cm[g], 16, 64));
                 cm[g] = pkmax_u16(cm[g], (uint32_t)__shfl_xor((int)cm[g], 32, 64));
             }
-            float sc[8];
-            bool nan_col = false;
+            float sc[8], si[8];
+            bool nan_lane = false;
 #pragma unroll
             for (int j = 0; j < 8; j++) {
                 const uint32_t m = (j & 1) ? (cm[j >> 1] >> 16) : (cm[j >> 1] & 0xFFFFu);
-                float si;
-                scale_from_amax_bits<FMT>(m, sc[j], si);
-                nan_col |= m > 0x7F80u;
-                if (rb == 0) {
-                    a.scale_col[(col0 + j) * rblocks + tr] = sc[j];
-                    a.scale_inv_col[(col0 + j) * rblocks + tr] = si;
-                }
+                scale_from_amax_bits<FMT>(m, sc[j], si[j]);
+                nan_lane |= m > 0x7F80u;
             }
+            // the tile's 128 column scales: one contiguous run of the
+            // block-row-major array; lanes of row group 0 store the scales,
+            // those of row group 1 the inverses, 8 columns (32 bytes) each
+            if (rb < 2) {
+                float* d = (rb == 0 ? a.scale_col : a.scale_inv_col) + tr * a.C + col0;
+                const float* w = rb == 0 ? sc : si;
+                *reinterpret_cast<float4*>(d) = make_float4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<float4*>(d + 4) = make_float4(w[4], w[5], w[6], w[7]);
+            }
+            const bool nan_col = __ballot(nan_lane) != 0;   // wave-uniform, as for the rows
             uint32_t t[8][8];
 #pragma unroll
             for (int h = 0; h < 8; h++) {

@@ -97,11 +97,15 @@ typedef enum {
  *   q_col      [C, R] codes (transposed layout), or NULL when not requested
  *   scale, scale_inv
  *              TENSOR:  1 float each
- *              1x128:   [R, C/128] (scales of the row layout)
+ *              1x128:   scales of the row layout, stored block-major as
+ *                       [C/128, R]: block (r, cb) covering
+ *                       x[r][cb*128 .. cb*128+127] at index cb*R + r
+ *                       (16-byte aligned)
  *              128x128: [R/128, C/128] (shared by both layouts)
  *   scale_col, scale_inv_col
- *              1x128 only: [C, R/128], scales of the col layout, block
- *              (c, rb) covering x[rb*128 .. rb*128+127][c]; ignored otherwise
+ *              1x128 only: scales of the col layout, stored block-major as
+ *              [R/128, C]: block (c, rb) covering x[rb*128 .. rb*128+127][c]
+ *              at index rb*C + c (16-byte aligned); ignored otherwise
  *   amax       optional (may be NULL): TENSOR: 1 float, the tensor's amax;
  *              ignored for block scaling
  */
@@ -146,6 +150,9 @@ fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols,
  *                (128 contraction elements) is
  *                scale_inv[(r / group) * stride_r + kb * stride_kb];
  *                group is 1 (1x128 blocks) or 128 (128x128 blocks).
+ *                The 1x128 scales fp8_quantize writes give, for the row
+ *                layout of an [R, C] source, stride_r = 1 and stride_kb = R,
+ *                for its col layout stride_r = 1 and stride_kb = C.
  * Both operands of one GEMM must be tensorwise or both block-scaled.
  */
 typedef struct {
