@@ -131,8 +131,13 @@ fp8k::GemmScale block_scale(const float* sinv, int64_t group, int64_t sr, int64_
     return fp8k::GemmScale{sinv, group, sr, sk};
 }
 
+// the GEMM kernels address one 256-row operand tile with 32-bit offsets
+constexpr int64_t kMaxContraction = int64_t(1) << 23;
+
 fp8_status do_gemm(const void* a, int fa, fp8k::GemmScale sa, const void* b, int fb, fp8k::GemmScale sb, int64_t I,
                    int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, hipStream_t st) {
+    if (K >= kMaxContraction)
+        return fail(FP8_ERR_SHAPE, "contraction length %lld: must be below 2^23", (long long)K);
     fp8k::GemmLaunch g;
     g.a = a;
     g.fa = fa;
@@ -214,6 +219,7 @@ fp8_status fp8_gemm(const void* a, fp8_format fa, fp8_gemm_scale sa, const void*
                     int64_t I, int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, void* stream) {
     FP8_TRY(check_dims("gemm I x J", I, J));
     FP8_TRY(check_dims("gemm K", K, 128));
+    if (K >= kMaxContraction) return fail(FP8_ERR_SHAPE, "contraction length %lld: must be below 2^23", (long long)K);
     if ((fa != FP8_E4M3 && fa != FP8_E5M2) || (fb != FP8_E4M3 && fb != FP8_E5M2))
         return fail(FP8_ERR_ENUM, "unknown operand format");
     FP8_TRY(check_ptr16("a", a));
@@ -270,6 +276,9 @@ size_t fp8_linear_workspace_bytes(int64_t N, int64_t K, int64_t M, fp8_recipe re
 static fp8_status check_linear_common(int64_t N, int64_t K, int64_t M, int recipe, void* ws, size_t ws_bytes) {
     FP8_TRY(check_dims("linear N x K", N, K));
     FP8_TRY(check_dims("linear M", M, 128));
+    // N, K and M are each the contraction of one of the three GEMMs
+    if (N >= kMaxContraction || K >= kMaxContraction || M >= kMaxContraction)
+        return fail(FP8_ERR_SHAPE, "linear dimensions must be below 2^23");
     if (recipe != FP8_RECIPE_TENSOR && recipe != FP8_RECIPE_BLOCK) return fail(FP8_ERR_ENUM, "unknown recipe %d", recipe);
     const size_t need = fp8_linear_workspace_bytes(N, K, M, static_cast<fp8_recipe>(recipe));
     if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

@@ -52,6 +52,9 @@ struct GemmLaunch {
 // tensorwise kernel (gemm_tensor.hip)
 int gemm_tensor_splits(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm_tensor(const GemmLaunch& l, int splits, hipStream_t stream);
+// block-scaled kernel (gemm_block.hip)
+int gemm_block_splits(int64_t I, int64_t J, int64_t K);
+hipError_t launch_gemm_block(const GemmLaunch& l, int splits, hipStream_t stream);
 int gemm_splits(int64_t I, int64_t J, int64_t K, bool block);
 size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);

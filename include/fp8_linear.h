@@ -80,7 +80,8 @@ enum { FP8_LAYOUT_ROW = 1, FP8_LAYOUT_COL = 2 };   /* bitmask */
 typedef enum {
     FP8_OK = 0,
     FP8_ERR_NULL = 1,            /* a required pointer is NULL */
-    FP8_ERR_SHAPE = 2,           /* a dimension is not a positive multiple of 128 */
+    FP8_ERR_SHAPE = 2,           /* a dimension is not a positive multiple of 128, or a
+                                    contraction length is 2^23 or more */
     FP8_ERR_ALIGN = 3,           /* a pointer is not 16-byte aligned */
     FP8_ERR_ENUM = 4,            /* unknown format / scaling / recipe / layout / flag */
     FP8_ERR_WORKSPACE = 5,       /* ws_bytes smaller than the query returned */
@@ -171,7 +172,9 @@ size_t fp8_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K);
  * multiplied by fl32(sA * sB) and rounded to bf16 (round to nearest even).
  * Block-scaled: every 128-long contraction block's fp32 partial sum is
  * multiplied by its two block factors and added to an fp32 accumulator.
- * format_a may be E4M3 or E5M2; format_b likewise.
+ * format_a may be E4M3 or E5M2; format_b likewise.  The contraction length
+ * K must be below 2^23 (FP8_ERR_SHAPE), which bounds the linear's N, K and M,
+ * each the contraction of one of its GEMMs.
  */
 fp8_status fp8_gemm(const void* a, fp8_format format_a, fp8_gemm_scale scale_a,
                     const void* b, fp8_format format_b, fp8_gemm_scale scale_b,

@@ -107,6 +107,10 @@ def test_gemm_argument_errors(L):
     assert g(sa=gs(group=3), sb=gs(group=1)) == ENUM
     assert g(sa=gs(p=None)) == NULL
     assert g(I=256, J=256, K=131072, wsb=0) == WORKSPACE
+    # 32-bit tile offsets: the contraction must stay below 2^23, checked
+    # before the workspace
+    assert g(K=1 << 23, wsb=0) == SHAPE
+    assert g(K=(1 << 23) - 128, wsb=0) == WORKSPACE
 
 
 def make_cache(L, M=256, K=256, recipe=0, bufs=None):
@@ -143,6 +147,12 @@ def test_cache_lifecycle_and_errors(L):
     assert L.fp8_linear_fwd(A, A, N, K, M, 0, h, 2, A, ctypes.byref(sx), None, A, wsb, None) == ENUM
     assert L.fp8_linear_fwd(A, A, N, K, M, 0, h, 1, A, ctypes.byref(sx), None, A, 16, None) == WORKSPACE
     assert L.fp8_linear_fwd(A, A, N, K, M, 0, None, -1, A, ctypes.byref(sx), None, A, wsb, None) == NULL
+    # every linear dimension is some GEMM's contraction: below 2^23
+    big = 1 << 23
+    assert L.fp8_linear_fwd(A, A, big, K, M, 0, None, -1, A, ctypes.byref(sx), ctypes.byref(qt()), A,
+                            1 << 40, None) == SHAPE
+    assert L.fp8_linear_bwd(A, N, K, big, 0, ctypes.byref(sx), None, ctypes.byref(qt()), ctypes.byref(qt()), A, A,
+                            A, 1 << 40, None) == SHAPE
     # backward through an empty cache
     dq = qt()
     r = L.fp8_linear_bwd(A, N, K, M, 0, ctypes.byref(sx), h, None, ctypes.byref(dq), A, A, A, wsb, None)

@@ -62,42 +62,51 @@ def test_gemm_tensorwise(fp8, I, J, K, fa, fb):
 
 
 BLOCK_CASES = [
-    # I, J, K, fa, fb, B layout ("row": 1x128 per row, "blk": 128x128, "blkT": 128x128 transposed)
-    (256, 256, 512, "e4m3", "e4m3", "blk"),
-    (384, 640, 256, "e4m3", "e4m3", "blk"),
-    (512, 256, 512, "e5m2", "e4m3", "blkT"),
-    (384, 384, 384, "e5m2", "e4m3", "row"),
-    (256, 128, 16384, "e5m2", "e4m3", "row"),   # split-K
+    # I, J, K, fa, fb, A layout, B layout:
+    #   "row":  1x128 factors [rows, K/128] row-major
+    #   "rowT": 1x128 factors stored block-major [K/128, rows] (what the quantizer writes)
+    #   "blk":  128x128 factors [rows/128, K/128];  "blkT": transposed
+    (256, 256, 512, "e4m3", "e4m3", "row", "blk"),
+    (384, 640, 256, "e4m3", "e4m3", "row", "blk"),
+    (512, 256, 512, "e5m2", "e4m3", "row", "blkT"),
+    (384, 384, 384, "e5m2", "e4m3", "row", "row"),
+    (256, 128, 16384, "e5m2", "e4m3", "row", "row"),     # split-K
+    (640, 384, 1152, "e5m2", "e4m3", "rowT", "rowT"),    # ragged last tile, block-major factors
+    (384, 512, 768, "e4m3", "e5m2", "blk", "rowT"),      # 128x128 factors on the A side
+    (128, 256, 4096, "e4m3", "e4m3", "rowT", "blkT"),    # one half-full tile, split-K
 ]
 
 
-@pytest.mark.parametrize("I,J,K,fa,fb,bl", BLOCK_CASES)
-def test_gemm_block(fp8, I, J, K, fa, fb, bl):
+def block_factors(layout, rows, KB, rng):
+    """(array, oracle.BlockScale, per-row factors [rows, KB]) for one operand."""
+    if layout == "row":
+        arr = rng.uniform(1e-3, 1e-1, (rows, KB)).astype(np.float32)
+        return arr, oracle.BlockScale(arr, 1, KB, 1), arr
+    if layout == "rowT":
+        arr = rng.uniform(1e-3, 1e-1, (KB, rows)).astype(np.float32)
+        return arr, oracle.BlockScale(arr, 1, 1, rows), arr.T
+    if layout == "blk":
+        arr = rng.uniform(1e-3, 1e-1, (rows // 128, KB)).astype(np.float32)
+        return arr, oracle.BlockScale(arr, 128, KB, 1), np.repeat(arr, 128, axis=0)
+    arr = rng.uniform(1e-3, 1e-1, (KB, rows // 128)).astype(np.float32)
+    return arr, oracle.BlockScale(arr, 128, 1, rows // 128), np.repeat(arr.T, 128, axis=0)
+
+
+@pytest.mark.parametrize("I,J,K,fa,fb,al,bl", BLOCK_CASES)
+def test_gemm_block(fp8, I, J, K, fa, fb, al, bl):
     rng = np.random.default_rng(I + J * 5 + K * 11)
     KB = K // 128
     A = rand_codes(fa, (I, K), rng)
     B = rand_codes(fb, (J, K), rng)
-    sA_arr = rng.uniform(1e-3, 1e-1, (I, KB)).astype(np.float32)
-    sA = oracle.BlockScale(sA_arr, 1, KB, 1)
-    if bl == "row":
-        sB_arr = rng.uniform(1e-3, 1e-1, (J, KB)).astype(np.float32)
-        sB = oracle.BlockScale(sB_arr, 1, KB, 1)
-        sB_full = sB_arr
-    elif bl == "blk":
-        sB_arr = rng.uniform(1e-3, 1e-1, (J // 128, KB)).astype(np.float32)
-        sB = oracle.BlockScale(sB_arr, 128, KB, 1)
-        sB_full = np.repeat(sB_arr, 128, axis=0)
-    else:
-        sB_arr = rng.uniform(1e-3, 1e-1, (KB, J // 128)).astype(np.float32)
-        sB = oracle.BlockScale(sB_arr, 128, 1, J // 128)
-        sB_full = np.repeat(sB_arr.T, 128, axis=0)
+    sA_arr, sA, sA_full = block_factors(al, I, KB, rng)
+    sB_arr, sB, sB_full = block_factors(bl, J, KB, rng)
     ref = oracle.gemm_block(A, fa, sA, B, fb, sB)
     tsa, tsb = dev(sA_arr), dev(sB_arr)
     c = fp8.gemm(dev(A), FMT[fa], fp8.gemm_scale(tsa, sA.group, sA.stride_r, sA.stride_kb),
                  dev(B), FMT[fb], fp8.gemm_scale(tsb, sB.group, sB.stride_r, sB.stride_kb))
     torch.cuda.synchronize()
-    hw = mfma_window_bound(A, fa, B, fb, (sA_arr, sB_full))
-    check_bf16(to_np_u16(c), ref, K, "block gemm %dx%dx%d %s" % (I, J, K, bl), hw)
+    hw = mfma_window_bound(A, fa, B, fb, (np.ascontiguousarray(sA_full), np.ascontiguousarray(sB_full)))
+    check_bf16(to_np_u16(c), ref, K, "block gemm %dx%dx%d %s %s" % (I, J, K, al, bl), hw)
 
 
 def test_gemm_identity_places_every_element(fp8):
