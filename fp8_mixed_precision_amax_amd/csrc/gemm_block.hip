@@ -50,7 +50,8 @@ constexpr int L = LA + LB + 1;              // + one 4-byte DMA of factors
 constexpr int RPK = 1024 / BK;              // rows per 1 KiB DMA block
 constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
 static_assert(SC_B + BN * 4 <= STAGE && STAGE % 1024 == 0, "stage");
-static_assert(S * STAGE <= 160 * 1024, "LDS");
+constexpr int SLICE = 1024;                 // per-wave epilogue slice: 8 rows x 64 bf16
+static_assert(S * STAGE + NW * SLICE <= 160 * 1024, "LDS");
 static_assert(LA % 2 == 0 && LB % 2 == 0, "odd DMA blocks alternate the swizzle");
 
 struct Args {
@@ -89,6 +90,7 @@ __device__ __forceinline__ bool item_at(const Args& g, int r, Item& it) {
 // s_waitcnt vmcnt(n) for a runtime n (rounded down to a supported value)
 __device__ __forceinline__ void wait_vm_n(int n) {
     if (n == L) wait_vm<L>();
+    else if (n == L + 8) wait_vm<L + 8>();
     else if (n == L + 16) wait_vm<L + 16>();
     else if (n >= 63) wait_vm<63>();
     else if (n >= 32) wait_vm<32>();
@@ -209,7 +211,9 @@ __device__ __forceinline__ void promote_one(v16f& acc, const v16f& p, float t) {
 
 template <int FA, int FB, bool SBROW>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
+    // separate objects: the epilogue's LDS traffic never aliases the stages
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sepi[NW * SLICE];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wi = wave & 3, wj = wave >> 2;
@@ -300,6 +304,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
     const uint32_t offA = (uint32_t)(arow * BK + ((ch ^ swz<BK>(arow)) << 4));
     const uint32_t offB = (uint32_t)(A_BYTES + brow * BK + ((ch ^ swz<BK>(brow)) << 4));
     const uint32_t offSA = (uint32_t)(SC_A + arow * 4);
+    const uint32_t epi_slice = lds_off(sepi) + (uint32_t)(wave * SLICE);
     const uint32_t offSB = SBROW ? (uint32_t)(SC_B + (wj * 64 + 4 * (lane >> 5)) * 4) : (uint32_t)(SC_B + wj * 64 * 4);
 
     v16f acc[2][2], p[2][2];
@@ -390,7 +395,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
                                         acc[mi][nj][4 * q + 3]);
             return 16;
         }
-        uint16_t* out = g.c + my_i * g.J + my_j;
+        // bf16 output through the wave's LDS slice, 8 rows at a time: row r
+        // holds 64 columns as 16-byte chunks, chunk c at (c ^ r) (the writes
+        // of 8 rows hit distinct banks); each store instruction then writes 8
+        // whole 128-byte row segments.  A wave's LDS operations execute in
+        // order, so a pass's read-back sees its writes and the next pass's
+        // writes follow the read.
+        uint2 w[2][2][4];
 #pragma unroll
         for (int mi = 0; mi < 2; mi++)
 #pragma unroll
@@ -401,12 +412,32 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
                     const __bf16 h1 = (__bf16)acc[mi][nj][4 * q + 1];
                     const __bf16 h2 = (__bf16)acc[mi][nj][4 * q + 2];
                     const __bf16 h3 = (__bf16)acc[mi][nj][4 * q + 3];
-                    uint2 w;
-                    w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                    w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                    *reinterpret_cast<uint2*>(out + (int64_t)mi * 32 * g.J + nj * 32 + 8 * q) = w;
+                    w[mi][nj][q].x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                    w[mi][nj][q].y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
                 }
-        return 16;
+        const int rw = frow & 7, gw = frow >> 3;          // writer: row in the pass, pass of its row
+        const uint32_t wbase = epi_slice + (uint32_t)(rw * 128 + (lane >> 5) * 8);
+        const int rr = lane >> 3, kr = lane & 7;          // reader: row, 16-byte chunk
+        const uint32_t raddr = epi_slice + (uint32_t)(rr * 128 + ((kr ^ rr) << 4));
+        uint8_t* ob = reinterpret_cast<uint8_t*>(g.c + (i0 + wi * 64 + rr) * g.J + j0 + wj * 64) + kr * 16;
+#pragma unroll
+        for (int mi = 0; mi < 2; mi++)
+#pragma unroll
+            for (int pg = 0; pg < 4; pg++) {
+                if (gw == pg) {
+#pragma unroll
+                    for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            const uint32_t wa = wbase + (uint32_t)((((nj * 4 + q) ^ rw) << 4));
+                            asm volatile("ds_write_b64 %0, %1" : : "v"(wa), "v"(w[mi][nj][q]) : "memory");
+                        }
+                }
+                u32x4 r;
+                asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(raddr) : "memory");
+                *reinterpret_cast<u32x4*>(ob + (int64_t)(mi * 32 + pg * 8) * g.J * 2) = r;
+            }
+        return 8;
     };
 
     while (c_ok) {
