@@ -351,11 +351,16 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
         float sa0_, sa1_;                                                                          \
         read_half_sa(fa_, fb_, sa0_, sa1_, a0_, a1_, b0_, b1_, sb_ + offSA);                       \
         __builtin_amdgcn_sched_barrier(0);                                                         \
+        /* each promotion issues behind one MFMA (MFMA first) */                                   \
         p[0][0] = mfma<FA, FB>(fb_[0], fa_[0], vzero);                                             \
         if (DEFER) FP8K_PROMOTE(1, 0, sa1_prev, sbr_prev, sb1_prev);                               \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+        __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         p[0][1] = mfma<FA, FB>(fb_[1], fa_[0], vzero);                                             \
         if (DEFER) FP8K_PROMOTE(1, 1, sa1_prev, sbr_prev, sb1_prev);                               \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+        __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         p[1][0] = mfma<FA, FB>(fb_[0], fa_[1], vzero);                                             \
         p[1][1] = mfma<FA, FB>(fb_[1], fa_[1], vzero);                                             \
@@ -367,13 +372,19 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
         __builtin_amdgcn_sched_barrier(0);                                                         \
         p[0][0] = mfma<FA, FB>(fb_[0], fa_[0], p[0][0]);                                           \
         p[0][1] = mfma<FA, FB>(fb_[1], fa_[0], p[0][1]);                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        /* blocks (0, *) completed two MFMAs earlier */                                            \
         p[1][0] = mfma<FA, FB>(fb_[0], fa_[1], p[1][0]);                                           \
-        p[1][1] = mfma<FA, FB>(fb_[1], fa_[1], p[1][1]);                                           \
-        __builtin_amdgcn_sched_barrier(0);                                                         \
         FP8K_PROMOTE(0, 0, sa0_, sbr_prev, sb1_prev);                                              \
-        FP8K_PROMOTE(0, 1, sa0_, sbr_prev, sb1_prev);                                              \
-        sa1_prev = sa1_;                                                                           \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+        __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                         \
+        p[1][1] = mfma<FA, FB>(fb_[1], fa_[1], p[1][1]);                                           \
+        FP8K_PROMOTE(0, 1, sa0_, sbr_prev, sb1_prev);                                              \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+        __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        sa1_prev = sa1_;                                                                           \
     } while (0)
 
     // write one item's accumulators; returns the vector-memory stores issued
