@@ -57,6 +57,8 @@ def parse():
                     help="after the steps, negate a 512 MiB fp16 tensor (counter calibration)")
     ap.add_argument("--summarize", metavar="PREFIX", help="summarize PREFIX_kernel_trace.csv / "
                     "PREFIX_counter_collection.csv of a profiled bench run and exit")
+    ap.add_argument("--recipe", choices=("tensor", "block"), default="tensor",
+                    help="with --summarize: which recipe's timed steps to summarize")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_PREFIX", "WRITE_PREFIX"),
                     help="per-stage HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE counter run "
                          "(each with --copy-reference), one line per stage, and exit")
@@ -64,19 +66,21 @@ def parse():
 
 
 SHAPES = [(512, 2048), (2048, 512)]
-KINDS = (("amax_partial_kernel", "amax"), ("cast_kernel", "cast"), ("gemm_kernel", "gemm"),
+KINDS = (("amax_partial_kernel", "amax"), ("cast_kernel", "cast"), ("gemm_block_kernel", "gemm"),
          ("gemm_tensor_kernel", "gemm"), ("splitk_reduce_kernel", "reduce"))
 COPY_BYTES = 2 * 512 * 1024 * 1024      # the --copy-reference kernel reads 512 MiB and writes 512 MiB
 
 
-def step_sequence(shapes):
+def step_sequence(shapes, recipe="tensor"):
     """Library calls of one step, in launch order, with the kernels each
-    launches (tensorwise recipe, weight requantized every step)."""
+    launches (weight requantized every step; a tensorwise quantize runs the
+    amax pass then the cast, a block-scaled one the cast alone)."""
+    q = ("cast",) if recipe == "block" else ("amax", "cast")
     seq = []
     for K, M in shapes:
         tag = "%dx%d" % (K, M)
-        seq += [("quant_w_" + tag, ("amax", "cast")), ("quant_x_" + tag, ("amax", "cast")),
-                ("gemm_fprop_" + tag, ("gemm",)), ("quant_dy_" + tag, ("amax", "cast")),
+        seq += [("quant_w_" + tag, q), ("quant_x_" + tag, q),
+                ("gemm_fprop_" + tag, ("gemm",)), ("quant_dy_" + tag, q),
                 ("gemm_dgrad_" + tag, ("gemm",)), ("gemm_wgrad_" + tag, ("gemm",))]
     return seq
 
@@ -91,7 +95,7 @@ def kernel_kind(name):
 
 
 def short_name(name):
-    return name.replace("void ", "").replace("fp8k::", "").replace("tensor::", "")
+    return name.replace("void ", "").replace("fp8k::", "").replace("tensor::", "").replace("block::", "")
 
 
 def source_digest():
@@ -107,11 +111,18 @@ def source_digest():
     return h.hexdigest()
 
 
-def walk_steps(disp, steps, warmup):
+def walk_steps(disp, steps, warmup, recipe="tensor"):
     """disp: [(kind, name, value)] of library dispatches in dispatch order.
-    Returns the timed steps as lists of (stage, kind, name, value)."""
-    seq = step_sequence(SHAPES)
+    Returns the timed steps as lists of (stage, kind, name, value).  The
+    block-scaled steps follow the tensorwise part of a run; they start at the
+    first 128x128 weight cast (cast_kernel<0, 2>)."""
+    seq = step_sequence(SHAPES, recipe)
     i, out = 0, []
+    if recipe == "block":
+        first = [k for k, d in enumerate(disp) if "cast_kernel<0, 2>" in d[1]]
+        if not first:
+            raise SystemExit("no block-scaled steps in this trace")
+        i = first[0]
     for s in range(warmup + steps):
         cur = []
         for stage, kinds in seq:
@@ -165,7 +176,7 @@ def traffic(fetch_prefix, write_prefix, steps, warmup):
         print("%s %d %s" % (stage, round(sum(v) / len(v)), digest))
 
 
-def summarize(prefix, steps, warmup):
+def summarize(prefix, steps, warmup, recipe="tensor"):
     out = []
     trace = prefix + "_kernel_trace.csv"
     stats = prefix + "_kernel_stats.csv"
@@ -186,7 +197,7 @@ def summarize(prefix, steps, warmup):
         disp = [(kernel_kind(r["Kernel_Name"]), short_name(r["Kernel_Name"]),
                  int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) for r in rows
                 if kernel_kind(r["Kernel_Name"])]
-        timed = walk_steps(disp, steps, warmup)
+        timed = walk_steps(disp, steps, warmup, recipe)
         per = collections.OrderedDict()
         for st in timed:
             for stage, kind, name, ns in st:
@@ -370,7 +381,7 @@ def cpu_baseline(shapes, tokens):
 def main():
     args = parse()
     if args.summarize:
-        summarize(args.summarize, args.steps, args.warmup)
+        summarize(args.summarize, args.steps, args.warmup, args.recipe)
         return
     if args.traffic:
         traffic(args.traffic[0], args.traffic[1], args.steps, args.warmup)
