@@ -10,8 +10,9 @@
 // Design
 //  - persistent: one workgroup per CU walks work items (256 x 256 output
 //    tile, split-K slice) dealt XCD by XCD (the dispatcher puts workgroup b on
-//    XCD b % 8) and rastered in groups of 2 tile rows, so the workgroups of one
-//    XCD share A and B tiles through its L2.
+//    XCD b % 8) and rastered in groups of tile rows (8 for wide outputs, 2
+//    for narrow ones), so the workgroups of one XCD share A and B tiles
+//    through its L2.
 //  - 8 waves, two per SIMD, wave tile 128 x 64 (4 x 2 blocks of
 //    v_mfma_f32_32x32x64_f8f6f4, 128 accumulator registers), all waves in
 //    lock step with one s_barrier per 64-long contraction step.
@@ -62,6 +63,7 @@ struct Args {
     uint16_t* c;
     float* part;          // split-K partials [splits][I][J]
     int splits, tiles_i, tiles_j, kpairs, items;
+    int gi;               // tile rows per raster group
 };
 
 struct Item {
@@ -74,19 +76,19 @@ __device__ __forceinline__ bool item_at(const Args& g, int r, Item& it) {
     if (Lg >= g.items) return false;
     const int tiles = g.tiles_i * g.tiles_j;
     const int z = Lg / tiles, t = Lg - z * tiles;
-    // groups of 2 tile rows: the workgroups of an XCD share B tiles across
-    // the group and A tiles along it; measured best of 2..32 on the K = 512
-    // output-heavy shapes (-8 %) and equal elsewhere
-    constexpr int GI = 2;
+    // raster groups of g.gi tile rows: the workgroups of an XCD share B tiles
+    // across the group and A tiles along it
+    const int GI = g.gi;
     const int per_group = GI * g.tiles_j, grp = t / per_group, local = t - grp * per_group;
     int rows = g.tiles_i - grp * GI;
     rows = rows < GI ? rows : GI;
     it.ti = grp * GI + local % rows;
     it.tj = local / rows;
     it.z = z;
-    // slices in units of 128 (two steps), so every item has an even count
-    it.kb = 2 * (int)(((int64_t)g.kpairs * z) / g.splits);
-    it.ke = 2 * (int)(((int64_t)g.kpairs * (z + 1)) / g.splits);
+    // slices in units of 128 (two steps), so every item has an even count;
+    // kpairs < 2^16 and splits <= 64 (contraction below 2^23): 32-bit math
+    it.kb = 2 * (g.kpairs * z / g.splits);
+    it.ke = 2 * (g.kpairs * (z + 1) / g.splits);
     return true;
 }
 
@@ -372,6 +374,11 @@ hipError_t launch_gemm_tensor(const GemmLaunch& l, int splits, hipStream_t strea
     g.tiles_j = (int)((l.J + BN - 1) / BN);
     g.kpairs = (int)(l.K / 128);
     g.items = g.tiles_i * g.tiles_j * splits;
+    // an XCD's 32 concurrent items cover 8 tile rows x 4 columns when the
+    // output is wide (8192 x 8192 x 16384: 955 -> 820 us against groups of
+    // 2), 16 x 2 when it has few tile columns (131072 x 512 x 2048: 139 us
+    // against 147 with groups of 8)
+    g.gi = g.tiles_j >= 16 ? 8 : 2;
     int grid = cu_count();
     if (grid > g.items) grid = g.items;
 #define FP8K_LAUNCH(FA, FB) \
