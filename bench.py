@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=int, default=131072)
-    ap.add_argument("--reps", type=int, default=20, help="repetitions per stage in the breakdown")
+    ap.add_argument("--reps", type=int, default=20, help="instrumented steps in the per-call breakdown")
     ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-stage breakdown")
@@ -242,9 +242,14 @@ def summarize(prefix, steps, warmup, recipe="tensor"):
 
 
 def stage_times(fp8, torch, layers, reps, recipe="tensor"):
-    """Average duration of each kernel-level call of one step, timed with
-    events on the stream the kernels run on (torch's current stream)."""
-    res = []
+    """Average duration of each kernel-level call of one step, in the step's
+    own call order: `reps` instrumented steps made of the same library calls
+    the linear launches (weight quantize, activation quantize, forward GEMM,
+    gradient quantize, data-gradient GEMM, weight-gradient GEMM, per layer),
+    with an event recorded between consecutive calls on the stream the kernels
+    run on (torch's current stream).  Each call thus runs after the call that
+    precedes it in a real step (e.g. a quantize reads while the previous
+    GEMM's output drains to HBM).  Returns (stages, ms per instrumented step)."""
     E4, E5 = fp8.E4M3, fp8.E5M2
     block = recipe == "block"
     act = fp8.SCALE_1x128 if block else fp8.SCALE_TENSOR
@@ -253,6 +258,7 @@ def stage_times(fp8, torch, layers, reps, recipe="tensor"):
     # two 1-byte layouts; block = one read + two layouts + fp32 scale and
     # inverse scale per 128-block of each layout (1x128) or per tile (128x128)
     act_b, w_b = (4 + 16 / 128, 4 + 8 / 16384) if block else (6, 6)
+    seq = []
     for L in layers:
         lin, N, K, M = L["lin"], L["N"], L["K"], L["M"]
         wq = lin.w_q
@@ -267,35 +273,43 @@ def stage_times(fp8, torch, layers, reps, recipe="tensor"):
             sx, sw, sdy = (fp8.gemm_scale(t.scale_inv) for t in (lin.saved_x, wq, lin.dy_q))
             swt, sdyc, sxc = sw, sdy, sx
         tag = "%dx%d" % (K, M)
-        calls = [
-            ("quant_x_" + tag, "quant", N * K * act_b, lambda: fp8.quantize(L["x"], E4, act, out=lin.saved_x)),
-            ("quant_w_" + tag, "quant", M * K * w_b, lambda: fp8.quantize(L["w"], E4, wsc, out=wq)),
-            ("gemm_fprop_" + tag, "gemm", (N, M, K), lambda: fp8.gemm(lin.saved_x.q_row, E4, sx, wq.q_row, E4, sw, out=L["y"])),
-            ("quant_dy_" + tag, "quant", N * M * act_b, lambda: fp8.quantize(L["dy"], E5, act, out=lin.dy_q)),
-            ("gemm_dgrad_" + tag, "gemm", (N, K, M), lambda: fp8.gemm(lin.dy_q.q_row, E5, sdy, wq.q_col, E4, swt, out=L["dx"])),
-            ("gemm_wgrad_" + tag, "gemm", (M, K, N), lambda: fp8.gemm(lin.dy_q.q_col, E5, sdyc, lin.saved_x.q_col, E4, sxc, out=L["dw"])),
+        seq += [
+            ("quant_w_" + tag, "quant", M * K * w_b, lambda L=L, wq=wq: fp8.quantize(L["w"], E4, wsc, out=wq)),
+            ("quant_x_" + tag, "quant", N * K * act_b, lambda L=L, lin=lin: fp8.quantize(L["x"], E4, act, out=lin.saved_x)),
+            ("gemm_fprop_" + tag, "gemm", (N, M, K),
+             lambda L=L, lin=lin, wq=wq, sx=sx, sw=sw: fp8.gemm(lin.saved_x.q_row, E4, sx, wq.q_row, E4, sw, out=L["y"])),
+            ("quant_dy_" + tag, "quant", N * M * act_b, lambda L=L, lin=lin: fp8.quantize(L["dy"], E5, act, out=lin.dy_q)),
+            ("gemm_dgrad_" + tag, "gemm", (N, K, M),
+             lambda L=L, lin=lin, wq=wq, sdy=sdy, swt=swt: fp8.gemm(lin.dy_q.q_row, E5, sdy, wq.q_col, E4, swt, out=L["dx"])),
+            ("gemm_wgrad_" + tag, "gemm", (M, K, N),
+             lambda L=L, lin=lin, sdyc=sdyc, sxc=sxc: fp8.gemm(lin.dy_q.q_col, E5, sdyc, lin.saved_x.q_col, E4, sxc,
+                                                             out=L["dw"])),
         ]
-        for name, kind, size, fn in calls:
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            if kind == "quant":
-                byts = int(size)
-                res.append({"stage": name, "ms": ms, "bytes": byts, "gbs": byts / ms / 1e6})
-            else:
-                I, J, Kc = size
-                flops = 2 * I * J * Kc
-                byts = I * Kc + J * Kc + 2 * I * J
-                res.append({"stage": name, "ms": ms, "flops": flops, "bytes": byts,
-                            "tflops": flops / ms / 1e9, "gbs": byts / ms / 1e6, "ai": flops / byts})
-    return res
+    for _ in range(2):
+        for _, _, _, fn in seq:
+            fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(reps)]
+    for r in range(reps):
+        for i, (_, _, _, fn) in enumerate(seq):
+            ev[r][i].record()
+            fn()
+        ev[r][-1].record()
+    torch.cuda.synchronize()
+    res = []
+    for i, (name, kind, size, _) in enumerate(seq):
+        ms = sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
+        if kind == "quant":
+            byts = int(size)
+            res.append({"stage": name, "ms": ms, "bytes": byts, "gbs": byts / ms / 1e6})
+        else:
+            I, J, Kc = size
+            flops = 2 * I * J * Kc
+            byts = I * Kc + J * Kc + 2 * I * J
+            res.append({"stage": name, "ms": ms, "flops": flops, "bytes": byts,
+                        "tflops": flops / ms / 1e9, "gbs": byts / ms / 1e6, "ai": flops / byts})
+    step_ms = sum(ev[r][0].elapsed_time(ev[r][-1]) for r in range(reps)) / reps
+    return res, step_ms
 
 
 def make_layers(fp8, torch, synth, N, recipe, dev):
@@ -416,7 +430,8 @@ def main():
     if args.no_breakdown:
         print(json.dumps({"ms_per_step": round(ms, 4), "value": round(value, 2)}), flush=True)
         return
-    stages = stage_times(fp8, torch, layers, args.reps)
+    stages, inst_ms = stage_times(fp8, torch, layers, args.reps)
+    print("instrumented steps: %.4f ms/step (events between calls)" % inst_ms, file=sys.stderr, flush=True)
     for s in stages:
         print("  %-24s %8.4f ms  %s" % (s["stage"], s["ms"],
                                         ("%.1f TFLOP/s %.0f GB/s" % (s["tflops"], s["gbs"])) if "flops" in s
@@ -431,7 +446,7 @@ def main():
         torch.cuda.empty_cache()
         blayers = make_layers(fp8, torch, synth, N, "block", dev)
         bms = time_steps(torch, blayers, args.steps, args.warmup)
-        bst = stage_times(fp8, torch, blayers, args.reps, "block")
+        bst, binst_ms = stage_times(fp8, torch, blayers, args.reps, "block")
         print("block scaling: %.4f ms/step" % bms, file=sys.stderr, flush=True)
         for st in bst:
             print("  %-24s %8.4f ms  %s" % (st["stage"], st["ms"],
@@ -441,6 +456,7 @@ def main():
         block = {"recipe": "X, dY 1x128 blocks; W 128x128 blocks", "value": round(flops / (bms / 1e3) / 1e12, 2),
                  "unit": "TFLOP/s", "ms_per_step": round(bms, 4),
                  "quantize_gbs": round(sum(st["bytes"] for st in bq) / sum(st["ms"] for st in bq) / 1e6, 1),
+                 "instrumented_ms_per_step": round(binst_ms, 4),
                  "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in st.items()} for st in bst],
                  "roofline": roofline_of(max(bst, key=lambda st: st["ms"]))}
         block["roofline"]["traffic"] = None
@@ -456,6 +472,7 @@ def main():
         "config": {"workload": "fp8 linear 512->2048 + 2048->512 fwd+bwd, N=%d, tensorwise current scaling" % N,
                    "tokens": N, "shapes": ["512x2048", "2048x512"], "recipe": "tensor"},
         "quantize_gbs": round(quant_gbs, 1),
+        "instrumented_ms_per_step": round(inst_ms, 4),
         "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in stages],
         "roofline": roofline_of(dom),
         "cpu_baseline": None,
