@@ -15,21 +15,28 @@
 //    through its L2.
 //  - 8 waves, two per SIMD, wave tile 128 x 64 (4 x 2 blocks of
 //    v_mfma_f32_32x32x64_f8f6f4, 128 accumulator registers), all waves in
-//    lock step with one s_barrier per 64-long contraction step.
+//    lock step with one s_barrier per 128-long contraction stage.
 //  - operands stream HBM -> LDS with buffer_load ... lds (LDS-DMA, no VGPR
-//    staging): 4 stages of 32 KiB, 3 in flight; each wave moves 4 KiB per
-//    stage through a buffer resource based at the tile (rows past I or J lie
-//    outside the resource and read as zero).  LDS rows are XOR-swizzled.
-//  - per step, after the barrier, a wave issues the DMA of the stage three
-//    ahead, then its 8 MFMAs with the fragments of the next step read in
-//    between (A fragment mi is reloaded right after its last MFMA; the two B
-//    fragments alternate between two register sets).
+//    staging): 2 stages of 64 KiB (A and B, 256 rows x 128 bytes each); each
+//    DMA instruction fills 8 whole 128-byte rows, so every cache line it
+//    touches is read in full (with 64-byte rows each instruction touched
+//    twice the lines and the L1 stalled the address unit: 8192 x 8192 x 16384
+//    830 -> 753 us).  Each wave moves 8 KiB per stage through a buffer
+//    resource based at the tile (rows past I or J lie outside the resource
+//    and read as zero).  LDS rows are XOR-swizzled.
+//  - a stage is two 64-long half steps of 8 MFMAs; the fragments of the next
+//    half step are read between the MFMAs (A fragment mi is reloaded right
+//    after its last MFMA; the two B fragments alternate between two register
+//    sets).  The first half reads the second half of the same rows; the
+//    second half starts with the hand-off of the next stage and reads its
+//    first half, and right after the barrier the wave issues the DMA of the
+//    stage after that into the buffer just consumed.
 //  - the hand-off of a stage is one s_waitcnt vmcnt(n) on the wave's own DMA
-//    (n counted exactly: the loads and epilogue stores issued after it) plus
-//    the barrier; fragment reads are inline assembly so the compiler adds no
+//    (n counted exactly: the epilogue stores issued after it) plus the
+//    barrier; fragment reads are inline assembly so the compiler adds no
 //    vmcnt(0) in front of them.  Their destination registers stay live
-//    operands of an lgkmcnt(0) wait (the next barrier, or the wait before the
-//    final epilogue), so no register with a load in flight is reused.
+//    operands of an lgkmcnt(0) wait (the next half step's, or the wait before
+//    the final epilogue), so no register with a load in flight is reused.
 //  - epilogue: each wave converts 32 rows at a time to bf16 into a private
 //    4 KiB LDS slice (chunk-major, (row ^ 2 chunk) swizzle: conflict-free
 //    writes and reads) and stores whole 128-byte row segments.
@@ -39,20 +46,21 @@
 namespace fp8k {
 namespace tensor {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int S = 4;                      // LDS stages (power of two)
-constexpr int D = S - 1;                  // stages in flight ahead of the one read
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int S = 2;                      // LDS stages (power of two)
+constexpr int D = S;                      // stages issued in the prologue
 constexpr int NW = 8;                     // waves
 constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
 constexpr int LA = A_BYTES / 1024 / NW;   // LDS-DMA instructions per wave per stage (A)
 constexpr int LB = B_BYTES / 1024 / NW;   // (B)
 constexpr int L = LA + LB;
-constexpr int RPK = 1024 / BK;            // rows per 1 KiB DMA block
+constexpr int RPK = 1024 / BK;            // rows per 1 KiB DMA block (whole 128-byte lines)
 constexpr int CPR = BK / 16;              // 16-byte chunks per LDS row
 constexpr int ECH = 8;                    // 16-byte chunks per epilogue row (64 bf16)
 constexpr int SLICE = 32 * ECH * 16;      // per-wave epilogue slice
 static_assert(S * STAGE + NW * SLICE <= 160 * 1024, "LDS");
 static_assert((S & (S - 1)) == 0, "S");
+static_assert(LA % 2 == 0 && LB % 2 == 0, "odd DMA blocks alternate the swizzle");
 
 struct Args {
     const uint8_t* a;
@@ -62,12 +70,12 @@ struct Args {
     int64_t I, J, K;
     uint16_t* c;
     float* part;          // split-K partials [splits][I][J]
-    int splits, tiles_i, tiles_j, kpairs, items;
+    int splits, tiles_i, tiles_j, kpairs, items;   // kpairs: contraction blocks of 128
     int gi;               // tile rows per raster group
 };
 
 struct Item {
-    int ti, tj, z, kb, ke;   // kb, ke: contraction steps of BK (even)
+    int ti, tj, z, kb, ke;   // kb, ke: contraction stages of BK = 128
 };
 
 __device__ __forceinline__ bool item_at(const Args& g, int r, Item& it) {
@@ -85,10 +93,9 @@ __device__ __forceinline__ bool item_at(const Args& g, int r, Item& it) {
     it.ti = grp * GI + local % rows;
     it.tj = local / rows;
     it.z = z;
-    // slices in units of 128 (two steps), so every item has an even count;
     // kpairs < 2^16 and splits <= 64 (contraction below 2^23): 32-bit math
-    it.kb = 2 * (g.kpairs * z / g.splits);
-    it.ke = 2 * (g.kpairs * (z + 1) / g.splits);
+    it.kb = g.kpairs * z / g.splits;
+    it.ke = g.kpairs * (z + 1) / g.splits;
     return true;
 }
 
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int wi = wave & 1, wj = wave >> 1;
     const uint32_t K = (uint32_t)g.K;
-    const uint32_t K16 = K * RPK;
+    const uint32_t KR = K * RPK;   // bytes of one DMA block's rows
 
     // ---- load cursor (uniform) ---------------------------------------------
     int l_round = 0;
@@ -122,8 +129,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     bool l_ok = item_at(g, 0, l_it);
     __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, 0);
     __amdgpu_buffer_rsrc_t rb = ra;
-    // lane offset inside a 16-row DMA block: row lane/4, swizzled chunk
-    const uint32_t loff = (uint32_t)(lane / CPR) * K + (uint32_t)(((lane % CPR) ^ swz<BK>(lane / CPR)) * 16);
+    // lane offset inside an 8-row DMA block: row lane/8, swizzled chunk; the
+    // odd blocks of a wave start at a row with bit 3 set, whose swizzle
+    // differs in chunk bit 2
+    const int lrow = lane / CPR;
+    const uint32_t loff0 = (uint32_t)lrow * K + (uint32_t)(((lane % CPR) ^ swz<BK>(lrow)) * 16);
+    const uint32_t loff1 = (uint32_t)lrow * K + (uint32_t)(((lane % CPR) ^ swz<BK>(lrow + RPK)) * 16);
     const uint32_t wrow_off = (uint32_t)(wave * LA * RPK) * K;   // this wave's first row of the tile
     uint32_t l_so = 0;   // buffer offset of the next stage to load
     int l_left = 0;      // stages left in the load item
@@ -143,11 +154,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
 #pragma unroll
         for (int p = 0; p < LA; p++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(uintptr_t)(dA + p * 1024),
-                                                     16, loff, __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * K16), 0, 0);
+                                                     16, (p & 1) ? loff1 : loff0,
+                                                     __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * KR), 0, 0);
 #pragma unroll
         for (int p = 0; p < LB; p++)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(uintptr_t)(dB + p * 1024),
-                                                     16, loff, __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * K16), 0, 0);
+                                                     16, (p & 1) ? loff1 : loff0,
+                                                     __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * KR), 0, 0);
         dma_off = (dma_off + STAGE) & (S * STAGE - 1);
         l_so += BK;
         if (--l_left == 0) {
@@ -164,7 +177,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
         }
     };
 
-    // ---- prologue: D stages in flight, stage 0 landed, its fragments read --
+    // ---- prologue: both stages in flight, stage 0 landed, the fragments of
+    // its first half read ------------------------------------------------------
 #pragma unroll
     for (int s = 0; s < D; s++) issue_stage();
     wait_vm<(D - 1) * L>();
@@ -179,7 +193,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     const int arow = wi * 128 + frow, brow = wj * 64 + frow;
     const int ch = (lane >> 5) * 2;
     const float t_tensor = g.sa[0] * g.sb[0];
-    // fragment rows in a stage: chunk ch (and ch+1 at ^16), +2048 per 32 rows
+    // fragment rows in a stage: chunk ch (ch+1 at ^16; the second 64-long
+    // half of the 128-byte row at ^64), +4096 per 32 rows
     const uint32_t offA = (uint32_t)(arow * BK + ((ch ^ swz<BK>(arow)) << 4));
     const uint32_t offB = (uint32_t)(A_BYTES + brow * BK + ((ch ^ swz<BK>(brow)) << 4));
 
@@ -194,13 +209,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     {
         const uint32_t a0 = smem0 + offA, a1 = a0 ^ 16u, b0 = smem0 + offB, b1 = b0 ^ 16u;
         fa[0] = ds_frag<0>(a0, a1);
-        fa[1] = ds_frag<2048>(a0, a1);
-        fa[2] = ds_frag<4096>(a0, a1);
-        fa[3] = ds_frag<6144>(a0, a1);
+        fa[1] = ds_frag<4096>(a0, a1);
+        fa[2] = ds_frag<8192>(a0, a1);
+        fa[3] = ds_frag<12288>(a0, a1);
         fb0[0] = ds_frag<0>(b0, b1);
-        fb0[1] = ds_frag<2048>(b0, b1);
+        fb0[1] = ds_frag<4096>(b0, b1);
     }
-    uint32_t rd_off = STAGE;   // stage buffer of the next fragments
+    uint32_t cur_off = 0;   // stage buffer being consumed
 
     // epilogue slice: (row r, chunk c) at c*512 + ((r ^ 2c) << 4)
     const uint32_t slice = lds_off(sepi) + (uint32_t)(wave * SLICE);
@@ -266,28 +281,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
         return 4 * 4;
     };
 
-    // One contraction step.  Stage k+1 (whose fragments this step reads) must
-    // have landed everywhere: wait for this wave's DMA of it -- the ops issued
-    // after it are the DMA of stage k+2 and any epilogue stores since -- then
-    // the barrier, which also retires every wave's reads of the buffer the
-    // DMA below overwrites (stage k-1's).
+    // A stage is two 64-long half steps of 8 MFMAs each; the fragments of
+    // the next half step are read while the current one's MFMAs run (A
+    // fragment mi is reloaded right after its last MFMA; the B fragments
+    // alternate between two register sets).  First half: its fragments come
+    // from the stage being consumed (second half of the rows, ^64).  Second
+    // half: the next stage must have landed everywhere -- wait for this
+    // wave's DMA of it (issued one stage earlier; only epilogue stores can
+    // follow it) and the barrier, which also retires every wave's reads of
+    // the consumed stage, whose buffer the DMA two stages ahead then fills.
 #define FP8K_MF(MI, FBC, FIRST)                                                                    \
     do {                                                                                           \
         acc[MI][0] = mfma<FA, FB>(FBC[0], fa[MI], (FIRST) ? vzero : acc[MI][0]);                  \
         acc[MI][1] = mfma<FA, FB>(FBC[1], fa[MI], (FIRST) ? vzero : acc[MI][1]);                  \
     } while (0)
-#define FP8K_STEP(FBC, FBN, FIRST)                                                                 \
+#define FP8K_HALF(FBC, FBN, FIRST, A0, B0)                                                         \
     do {                                                                                           \
-        wait_vm_n(L + st_cur);                                                                     \
-        st_cur = 0;                                                                                \
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"                                           \
-                     : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(FBC[0]), "+v"(FBC[1]) \
-                     :                                                                             \
-                     : "memory");                                                                  \
-        issue_stage();                                                                             \
-        const uint32_t sb_ = smem0 + rd_off;                                                       \
-        rd_off = (rd_off + STAGE) & (S * STAGE - 1);                                               \
-        const uint32_t a0_ = sb_ + offA, a1_ = a0_ ^ 16u, b0_ = sb_ + offB, b1_ = b0_ ^ 16u;       \
+        const uint32_t a0_ = (A0), a1_ = a0_ ^ 16u, b0_ = (B0), b1_ = b0_ ^ 16u;                   \
         FP8K_MF(0, FBC, FIRST);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         fa[0] = ds_frag<0>(a0_, a1_);                                                              \
@@ -295,17 +305,34 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
         __builtin_amdgcn_sched_barrier(0);                                                         \
         FP8K_MF(1, FBC, FIRST);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
-        fa[1] = ds_frag<2048>(a0_, a1_);                                                           \
-        FBN[1] = ds_frag<2048>(b0_, b1_);                                                          \
+        fa[1] = ds_frag<4096>(a0_, a1_);                                                           \
+        FBN[1] = ds_frag<4096>(b0_, b1_);                                                          \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         FP8K_MF(2, FBC, FIRST);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
-        fa[2] = ds_frag<4096>(a0_, a1_);                                                           \
+        fa[2] = ds_frag<8192>(a0_, a1_);                                                           \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         FP8K_MF(3, FBC, FIRST);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
-        fa[3] = ds_frag<6144>(a0_, a1_);                                                           \
+        fa[3] = ds_frag<12288>(a0_, a1_);                                                          \
         __builtin_amdgcn_sched_barrier(0);                                                         \
+    } while (0)
+#define FP8K_STAGE(FIRST)                                                                          \
+    do {                                                                                           \
+        asm volatile("s_waitcnt lgkmcnt(0)"                                                        \
+                     : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb0[0]), "+v"(fb0[1]) \
+                     :                                                                             \
+                     : "memory");                                                                  \
+        FP8K_HALF(fb0, fb1, FIRST, (smem0 + cur_off + offA) ^ 64u, (smem0 + cur_off + offB) ^ 64u);  \
+        wait_vm_n(st_cur);                                                                         \
+        st_cur = 0;                                                                                \
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"                                           \
+                     : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb1[0]), "+v"(fb1[1]) \
+                     :                                                                             \
+                     : "memory");                                                                  \
+        issue_stage();                                                                             \
+        cur_off ^= (uint32_t)STAGE;                                                                \
+        FP8K_HALF(fb1, fb0, false, smem0 + cur_off + offA, smem0 + cur_off + offB);                \
     } while (0)
 
     const v16f vzero = {};
@@ -314,24 +341,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     while (c_ok) {
         Item n_it;
         const bool more = item_at(g, c_round + 1, n_it);
-        const int nsteps = c_it.ke - c_it.kb;   // even, >= 2
+        const int nstages = c_it.ke - c_it.kb;   // >= 1
         if (have_prev) st_cur += epilogue(p_it);
-        FP8K_STEP(fb0, fb1, true);
-        for (int s = 1; s < nsteps - 1; s += 2) {
-            FP8K_STEP(fb1, fb0, false);
-            FP8K_STEP(fb0, fb1, false);
-        }
-        // after the last item the fragments this reads are unused (their
-        // stage is a re-read of the last one); reading anyway keeps a single
-        // definition of every fragment register
-        FP8K_STEP(fb1, fb0, false);
+        FP8K_STAGE(true);
+        // after the last item the fragments the last half step reads are
+        // unused (their stage is a re-read of the last one); reading anyway
+        // keeps a single definition of every fragment register
+        for (int s = 1; s < nstages; s++) FP8K_STAGE(false);
         p_it = c_it;
         have_prev = true;
         c_it = n_it;
         c_ok = more;
         c_round++;
     }
-#undef FP8K_STEP
+#undef FP8K_STAGE
+#undef FP8K_HALF
 #undef FP8K_MF
     // The last step's fragment reads (of a re-read stage) are dead but still
     // in flight: let them land before the epilogue's temporaries can reuse
