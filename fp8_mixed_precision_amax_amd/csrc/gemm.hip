@@ -45,26 +45,31 @@ int cu_count() {
     return cache[dev];
 }
 
-int gemm_splits(int64_t I, int64_t J, int64_t K, bool block) {
-    return block ? gemm_block_splits(I, J, K) : gemm_tensor_splits(I, J, K);
-}
-
 size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K) {
-    const int a = gemm_splits(I, J, K, false), b = gemm_splits(I, J, K, true);
-    const int s = a > b ? a : b;
+    // the largest split count any of the kernels would use for this shape
+    int s = gemm_tensor_splits(I, J, K);
+    const int b = gemm_block_splits(I, J, K), w = gemm_block_wide_splits(I, J, K);
+    s = s > b ? s : b;
+    s = s > w ? s : w;
     return s > 1 ? (size_t)s * (size_t)I * (size_t)J * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream) {
     const bool block = l.sa.group != 0;
-    const int splits = gemm_splits(l.I, l.J, l.K, block);
+    int splits;
+    hipError_t e;
     if (!block) {
-        hipError_t e = launch_gemm_tensor(l, splits, stream);
-        if (e != hipSuccess || splits == 1) return e;
+        splits = gemm_tensor_splits(l.I, l.J, l.K);
+        e = launch_gemm_tensor(l, splits, stream);
+    } else if (l.sb.group == 128) {
+        // B factors shared by 128-row groups (a 128x128-block weight)
+        splits = gemm_block_wide_splits(l.I, l.J, l.K);
+        e = launch_gemm_block_wide(l, splits, stream);
     } else {
-        hipError_t e = launch_gemm_block(l, splits, stream);
-        if (e != hipSuccess || splits == 1) return e;
+        splits = gemm_block_splits(l.I, l.J, l.K);
+        e = launch_gemm_block(l, splits, stream);
     }
+    if (e != hipSuccess || splits == 1) return e;
     const int64_t n4 = l.I * l.J / 4;
     int64_t blocks = (n4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;

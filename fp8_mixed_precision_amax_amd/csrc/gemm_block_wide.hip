@@ -1,0 +1,434 @@
+// Block-scaled FP8 GEMM for a B operand whose factors are shared by 128-row
+// groups (a 128x128-block weight: the forward and data-gradient GEMMs of the
+// Float8BlockScaling linear).  C[i][j] = sum_kb sA[i][kb] sB[j/128][kb] P_kb[i][j],
+// P_kb the fp32 partial sum of 128-long contraction block kb; BF16 output, or
+// fp32 partial sums for split-K.
+//
+// Method: as gemm_block.hip (Float8BlockScaling, TransformerEngine issue
+// 2852; "Native FP8 MLP reconstruction", implementation paragraph): every
+// block's partial sum is multiplied by its two factors and added to an fp32
+// accumulator, acc = fma(P_kb, sA * sB, acc).
+//
+// Design (the tensorwise kernel's tile with block-major promotion)
+//  - persistent, 8 waves (two per SIMD), output tile 256 x 256, wave tile
+//    128 x 64: 4 x 2 blocks of v_mfma_f32_32x32x64_f8f6f4.  Per stage (one
+//    128-block) a wave reads the B fragments of both 64-long halves once and
+//    walks its four 32-row blocks mi: the 4 MFMAs of (mi, *) over both halves
+//    into two 16-register partial sums, then their promotion.  Only 32
+//    registers of partial sums are live, so the 128 accumulators fit two
+//    waves per SIMD; the A fragments of the next mi are read while the MFMAs
+//    of the current one run, and the other wave of the SIMD issues MFMAs
+//    while this one promotes.  Against a 256 x 128 tile this moves a third
+//    less L2 -> LDS data and reads 30 % fewer LDS fragment bytes per FLOP.
+//  - a wave's 64 columns lie in one 128-row group of B, so its B factor is
+//    one value per stage (one FMA per element promotes).
+//  - 2 stages of 66 KiB (A and B 256 rows x 128 bytes: every DMA instruction
+//    reads whole 128-byte lines; then the fp32 factors of the 256 + 256
+//    rows, one 4-byte DMA per wave); hand-off by exact s_waitcnt vmcnt(n) on
+//    the wave's own DMA plus s_barrier at the end of each stage, after which
+//    the DMA two stages ahead fills the buffer just consumed.
+//  - bf16 epilogue through a 2 KiB per-wave LDS slice, 16 rows at a time
+//    (chunk c of row r at c ^ (r/2 mod 8): conflict-free 8-byte writes of 16
+//    rows), each store instruction writing 8 whole 128-byte row segments.
+#include "gemm_common.hpp"
+#include "internal.hpp"
+
+namespace fp8k {
+namespace blockw {
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int S = 2;                        // LDS stages
+constexpr int NW = 8;                       // waves
+constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+constexpr int SC_A = A_BYTES + B_BYTES;     // fp32 factors of the A rows
+constexpr int SC_B = SC_A + BM * 4;         // fp32 factors of the B rows
+constexpr int STAGE = SC_B + BN * 4;        // 66 KiB
+constexpr int LA = A_BYTES / 1024 / NW;     // LDS-DMA instructions per wave per stage (A)
+constexpr int LB = B_BYTES / 1024 / NW;     // (B)
+constexpr int L = LA + LB + 1;              // + one 4-byte DMA of factors
+constexpr int RPK = 1024 / BK;              // rows per 1 KiB DMA block
+constexpr int CPR = BK / 16;                // 16-byte chunks per LDS row
+constexpr int SLICE = 2048;                 // per-wave epilogue slice: 16 rows x 64 bf16
+static_assert(STAGE % 1024 == 0, "stage");
+static_assert(S * STAGE + NW * SLICE <= 160 * 1024, "LDS");
+static_assert(LA % 2 == 0 && LB % 2 == 0, "odd DMA blocks alternate the swizzle");
+
+struct Args {
+    const uint8_t* a;
+    const uint8_t* b;
+    GemmScale sa, sb;
+    int64_t I, J, K;
+    uint16_t* c;
+    float* part;          // split-K partials [splits][I][J]
+    int splits, tiles_i, tiles_j, ktiles, items;
+    int gi;               // tile rows per raster group
+};
+
+struct Item {
+    int ti, tj, z, kb, ke;   // kb, ke: 128-blocks of the contraction
+};
+
+__device__ __forceinline__ bool item_at(const Args& g, int r, Item& it) {
+    const int G = gridDim.x, b = blockIdx.x;
+    const int Lg = r * G + ((G & 7) == 0 ? (b & 7) * (G >> 3) + (b >> 3) : b);
+    if (Lg >= g.items) return false;
+    const int tiles = g.tiles_i * g.tiles_j;
+    const int z = Lg / tiles, t = Lg - z * tiles;
+    const int GI = g.gi;
+    const int per_group = GI * g.tiles_j, grp = t / per_group, local = t - grp * per_group;
+    int rows = g.tiles_i - grp * GI;
+    rows = rows < GI ? rows : GI;
+    it.ti = grp * GI + local % rows;
+    it.tj = local / rows;
+    it.z = z;
+    // ktiles < 2^16 and splits <= 64 (contraction below 2^23): 32-bit math
+    it.kb = g.ktiles * z / g.splits;
+    it.ke = g.ktiles * (z + 1) / g.splits;
+    return true;
+}
+
+// s_waitcnt vmcnt(n) for a runtime n (rounded down to a supported value)
+__device__ __forceinline__ void wait_vm_n(int n) {
+    if (n >= 32) wait_vm<32>();
+    else if (n >= 16) wait_vm<16>();
+    else wait_vm<0>();
+}
+
+// Fragments of a stage's first A block and of both B blocks (both 64-long
+// halves each: the second half of a swizzled row is at address ^ 64), the A
+// factors of the lane's four rows and the wave's B factor, issued and waited
+// for in one asm statement.  a0/a1, b0/b1: the lane's two 16-byte chunks.
+__device__ __forceinline__ void read_stage(v8i (&fa)[2], v8i (&fb)[2][2], float (&sa)[4], float& sb, uint32_t a0,
+                                           uint32_t a1, uint32_t b0, uint32_t b1, uint32_t pa, uint32_t pb) {
+    const uint32_t a2 = a0 ^ 64u, a3 = a1 ^ 64u, b2 = b0 ^ 64u, b3 = b1 ^ 64u;
+    u32x4 x0, x1, x2, x3, y0, y1, y2, y3, y4, y5, y6, y7;
+    asm volatile(
+        "ds_read_b128 %0, %17 offset:0\n\t"
+        "ds_read_b128 %1, %18 offset:0\n\t"
+        "ds_read_b128 %2, %19 offset:0\n\t"
+        "ds_read_b128 %3, %20 offset:0\n\t"
+        "ds_read_b128 %4, %21 offset:0\n\t"
+        "ds_read_b128 %5, %22 offset:0\n\t"
+        "ds_read_b128 %6, %23 offset:0\n\t"
+        "ds_read_b128 %7, %24 offset:0\n\t"
+        "ds_read_b128 %8, %21 offset:4096\n\t"
+        "ds_read_b128 %9, %22 offset:4096\n\t"
+        "ds_read_b128 %10, %23 offset:4096\n\t"
+        "ds_read_b128 %11, %24 offset:4096\n\t"
+        "ds_read_b32 %12, %25 offset:0\n\t"
+        "ds_read_b32 %13, %25 offset:128\n\t"
+        "ds_read_b32 %14, %25 offset:256\n\t"
+        "ds_read_b32 %15, %25 offset:384\n\t"
+        "ds_read_b32 %16, %26\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(y0), "=&v"(y1), "=&v"(y2), "=&v"(y3), "=&v"(y4),
+          "=&v"(y5), "=&v"(y6), "=&v"(y7), "=&v"(sa[0]), "=&v"(sa[1]), "=&v"(sa[2]), "=&v"(sa[3]), "=&v"(sb)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1), "v"(b2), "v"(b3), "v"(pa), "v"(pb)
+        : "memory");
+    fa[0] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    fa[1] = __builtin_bit_cast(v8i, __builtin_shufflevector(x2, x3, 0, 1, 2, 3, 4, 5, 6, 7));
+    fb[0][0] = __builtin_bit_cast(v8i, __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7));
+    fb[0][1] = __builtin_bit_cast(v8i, __builtin_shufflevector(y2, y3, 0, 1, 2, 3, 4, 5, 6, 7));
+    fb[1][0] = __builtin_bit_cast(v8i, __builtin_shufflevector(y4, y5, 0, 1, 2, 3, 4, 5, 6, 7));
+    fb[1][1] = __builtin_bit_cast(v8i, __builtin_shufflevector(y6, y7, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Both halves of one A block's fragments (a0, a1: the lane's two chunks of
+// the block's first half).
+__device__ __forceinline__ void read_a(v8i (&fa)[2], uint32_t a0, uint32_t a1) {
+    const uint32_t a2 = a0 ^ 64u, a3 = a1 ^ 64u;
+    u32x4 x0, x1, x2, x3;
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+    fa[0] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+    fa[1] = __builtin_bit_cast(v8i, __builtin_shufflevector(x2, x3, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_block_wide_kernel(Args g) {
+    // separate objects: the epilogue's LDS traffic never aliases the stages
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t sepi[NW * SLICE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int wi = wave & 1, wj = wave >> 1;
+    const uint32_t K = (uint32_t)g.K;
+    const uint32_t KR = K * RPK;   // bytes of one DMA block's rows
+
+    // ---- load cursor (uniform) ---------------------------------------------
+    int l_round = 0;
+    Item l_it;
+    bool l_ok = item_at(g, 0, l_it);
+    __amdgpu_buffer_rsrc_t ra = make_rsrc(g.a, 0);
+    __amdgpu_buffer_rsrc_t rb = ra;
+    // lane offset inside an 8-row DMA block: row lane/8, swizzled chunk; the
+    // odd blocks of a wave start at a row with bit 3 set, whose swizzle
+    // differs in chunk bit 2
+    const int lrow = lane / CPR;
+    const uint32_t loff0 = (uint32_t)lrow * K + (uint32_t)(((lane % CPR) ^ swz<BK>(lrow)) * 16);
+    const uint32_t loff1 = (uint32_t)lrow * K + (uint32_t)(((lane % CPR) ^ swz<BK>(lrow + RPK)) * 16);
+    const uint32_t wrow_off = (uint32_t)(wave * LA * RPK) * K;   // this wave's first row of the tile
+    uint32_t l_so = 0;   // buffer offset of the next stage to load
+    int l_left = 0;      // stages left in the load item
+    // factor DMA: waves 0-3 move A rows 64w .. 64w+63, waves 4-7 B rows
+    // 64(w-4) .. 64(w-4)+63
+    const bool sc_is_a = wave < 4;
+    const GemmScale& gs = sc_is_a ? g.sa : g.sb;
+    const int sc_row = (wave & 3) * 64 + lane;
+    const uint32_t sc_lds = (uint32_t)((sc_is_a ? SC_A : SC_B) + (wave & 3) * 256);
+    const float* l_ps = g.sa.sinv;
+    auto set_load_item = [&]() __attribute__((always_inline)) {
+        const int64_t i0 = (int64_t)l_it.ti * BM, j0 = (int64_t)l_it.tj * BN;
+        ra = make_rsrc(g.a + i0 * g.K, (g.I - i0 < BM ? g.I - i0 : BM) * g.K);
+        rb = make_rsrc(g.b + j0 * g.K, (g.J - j0 < BN ? g.J - j0 : BN) * g.K);
+        l_so = wrow_off + (uint32_t)l_it.kb * BK;
+        l_left = l_it.ke - l_it.kb;
+        int64_t r = (sc_is_a ? i0 : j0) + sc_row;
+        const int64_t rmax = (sc_is_a ? g.I : g.J) - 1;
+        r = r < rmax ? r : rmax;
+        l_ps = gs.sinv + (gs.group == 1 ? r : r >> 7) * gs.stride_r + (int64_t)l_it.kb * gs.stride_kb;   // group 1 or 128
+    };
+    if (l_ok) set_load_item();
+    const uint32_t smem0 = lds_off(smem);
+    uint32_t dma_off = 0;   // stage buffer the next DMA fills
+    auto issue_stage = [&]() __attribute__((always_inline)) {
+        const uint32_t dA = smem0 + dma_off + (uint32_t)(wave * LA * 1024);
+        const uint32_t dB = smem0 + dma_off + (uint32_t)(A_BYTES + wave * LB * 1024);
+#pragma unroll
+        for (int p = 0; p < LA; p++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(uintptr_t)(dA + p * 1024),
+                                                     16, (p & 1) ? loff1 : loff0,
+                                                     __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * KR), 0, 0);
+#pragma unroll
+        for (int p = 0; p < LB; p++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(uintptr_t)(dB + p * 1024),
+                                                     16, (p & 1) ? loff1 : loff0,
+                                                     __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * KR), 0, 0);
+        __builtin_amdgcn_global_load_lds(l_ps, (__attribute__((address_space(3))) void*)(uintptr_t)(smem0 + dma_off + sc_lds),
+                                         4, 0, 0);
+        dma_off = dma_off == 0 ? (uint32_t)STAGE : 0u;
+        if (--l_left == 0) {
+            if (l_ok && item_at(g, l_round + 1, l_it)) {
+                l_round++;
+                set_load_item();
+            } else {
+                // past the last item: keep re-reading its last stage into
+                // buffers nobody reads, so every stage issues the same loads
+                l_ok = false;
+                l_left = 1;
+            }
+        } else {
+            l_so += BK;
+            l_ps += gs.stride_kb;
+        }
+    };
+
+    // ---- prologue: both stages in flight, stage 0 landed ----------------------
+    issue_stage();
+    issue_stage();
+    wait_vm<L>();
+    barrier_lds();
+
+    int c_round = 0;
+    Item c_it;
+    bool c_ok = item_at(g, 0, c_it);
+    int st_cur = 0;   // epilogue stores issued since the last stage wait
+
+    const int frow = lane & 31;
+    const int arow = wi * 128 + frow, brow = wj * 64 + frow;
+    const int ch = (lane >> 5) * 2;
+    // fragment rows in a stage: chunk ch (ch+1 at ^16; the second 64-long
+    // half at ^64), +4096 bytes per 32 rows
+    const uint32_t offA = (uint32_t)(arow * BK + ((ch ^ swz<BK>(arow)) << 4));
+    const uint32_t offB = (uint32_t)(A_BYTES + brow * BK + ((ch ^ swz<BK>(brow)) << 4));
+    const uint32_t offSA = (uint32_t)(SC_A + arow * 4);
+    const uint32_t offSB = (uint32_t)(SC_B + wj * 64 * 4);
+    const uint32_t epi_slice = lds_off(sepi) + (uint32_t)(wave * SLICE);
+
+    v16f acc[4][2];
+#pragma unroll
+    for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+        for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[mi][nj][v] = 0.0f;
+    const v16f vzero = {};
+    uint32_t cur_off = 0;   // stage buffer being consumed
+
+    // write one item's accumulators; returns the vector-memory stores issued
+    auto epilogue = [&](const Item& it) __attribute__((always_inline)) -> int {
+        const int64_t i0 = (int64_t)it.ti * BM, j0 = (int64_t)it.tj * BN;
+        // validity is uniform per wave (I and J are multiples of 128)
+        if (i0 + wi * 128 >= g.I || j0 + wj * 64 >= g.J) return 0;
+        if (g.splits > 1) {
+            float* out = g.part + (int64_t)it.z * g.I * g.J + (i0 + arow) * g.J + j0 + wj * 64 + 4 * (lane >> 5);
+#pragma unroll
+            for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+                for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        *reinterpret_cast<float4*>(out + (int64_t)mi * 32 * g.J + nj * 32 + 8 * q) =
+                            make_float4(acc[mi][nj][4 * q], acc[mi][nj][4 * q + 1], acc[mi][nj][4 * q + 2],
+                                        acc[mi][nj][4 * q + 3]);
+            return 32;
+        }
+        // bf16 through the wave's LDS slice, 16 rows at a time: row r holds
+        // 64 columns as 16-byte chunks, chunk c at (c ^ (r/2 mod 8)); a pass's
+        // read-back sees its writes and the next pass's writes follow the
+        // read (a wave's LDS operations execute in order)
+        uint2 w[4][2][4];
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+            for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const __bf16 h0 = (__bf16)acc[mi][nj][4 * q];
+                    const __bf16 h1 = (__bf16)acc[mi][nj][4 * q + 1];
+                    const __bf16 h2 = (__bf16)acc[mi][nj][4 * q + 2];
+                    const __bf16 h3 = (__bf16)acc[mi][nj][4 * q + 3];
+                    w[mi][nj][q].x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                    w[mi][nj][q].y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                }
+        const int rw = frow & 15, gw = frow >> 4;         // writer: row in the pass, pass of its row
+        const uint32_t wbase = epi_slice + (uint32_t)(rw * 128 + (lane >> 5) * 8);
+        const int rr = lane >> 3, kr = lane & 7;          // reader: rows rr and rr + 8, chunk kr
+        const uint32_t ra0 = epi_slice + (uint32_t)(rr * 128 + ((kr ^ ((rr >> 1) & 7)) << 4));
+        const uint32_t ra1 = epi_slice + (uint32_t)((rr + 8) * 128 + ((kr ^ (((rr + 8) >> 1) & 7)) << 4));
+        uint8_t* ob = reinterpret_cast<uint8_t*>(g.c + (i0 + wi * 128 + rr) * g.J + j0 + wj * 64) + kr * 16;
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+            for (int pg = 0; pg < 2; pg++) {
+                if (gw == pg) {
+#pragma unroll
+                    for (int nj = 0; nj < 2; nj++)
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            const uint32_t wa = wbase + (uint32_t)((((nj * 4 + q) ^ ((rw >> 1) & 7)) << 4));
+                            asm volatile("ds_write_b64 %0, %1" : : "v"(wa), "v"(w[mi][nj][q]) : "memory");
+                        }
+                }
+                u32x4 r0, r1;
+                asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                             : "=&v"(r0), "=&v"(r1)
+                             : "v"(ra0), "v"(ra1)
+                             : "memory");
+                uint8_t* o = ob + (int64_t)(mi * 32 + pg * 16) * g.J * 2;
+                *reinterpret_cast<u32x4*>(o) = r0;
+                *reinterpret_cast<u32x4*>(o + (int64_t)8 * g.J * 2) = r1;
+            }
+        return 16;
+    };
+
+    // One 128-block.  Then the hand-off: wait for this wave's DMA of the next
+    // stage (only epilogue stores can follow it), the barrier (every wave is
+    // done with the consumed stage), and the DMA two stages ahead into it.
+#define FP8K_BLOCK_MI(MI)                                                                          \
+    do {                                                                                           \
+        v16f p0 = mfma<FA, FB>(fb[0][0], fa[0], vzero);                                            \
+        v16f p1 = mfma<FA, FB>(fb[1][0], fa[0], vzero);                                            \
+        p0 = mfma<FA, FB>(fb[0][1], fa[1], p0);                                                    \
+        p1 = mfma<FA, FB>(fb[1][1], fa[1], p1);                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        if ((MI) < 3) read_a(fa, sb_ + offA + (uint32_t)(((MI) + 1) * 4096), (sb_ + offA + (uint32_t)(((MI) + 1) * 4096)) ^ 16u); \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        const float t_ = sa[MI] * sbv;                                                             \
+        _Pragma("unroll") for (int v = 0; v < 16; v++) {                                           \
+            acc[MI][0][v] = __builtin_fmaf(p0[v], t_, acc[MI][0][v]);                              \
+            acc[MI][1][v] = __builtin_fmaf(p1[v], t_, acc[MI][1][v]);                              \
+        }                                                                                          \
+        /* pin the promotion here: otherwise the compiler sinks it below the */                   \
+        /* stage's later MFMAs and keeps every block's partial sums live     */                   \
+        asm volatile("" : "+v"(acc[MI][0]), "+v"(acc[MI][1]));                                     \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+    } while (0)
+#define FP8K_STAGE()                                                                               \
+    do {                                                                                           \
+        const uint32_t sb_ = smem0 + cur_off;                                                      \
+        v8i fa[2], fb[2][2];                                                                       \
+        float sa[4], sbv;                                                                          \
+        read_stage(fa, fb, sa, sbv, sb_ + offA, (sb_ + offA) ^ 16u, sb_ + offB, (sb_ + offB) ^ 16u, \
+                   sb_ + offSA, sb_ + offSB);                                                      \
+        __builtin_amdgcn_sched_barrier(0);                                                         \
+        FP8K_BLOCK_MI(0);                                                                          \
+        FP8K_BLOCK_MI(1);                                                                          \
+        FP8K_BLOCK_MI(2);                                                                          \
+        FP8K_BLOCK_MI(3);                                                                          \
+        wait_vm_n(st_cur);                                                                         \
+        st_cur = 0;                                                                                \
+        asm volatile("s_barrier" ::: "memory");                                                    \
+        issue_stage();                                                                             \
+        cur_off ^= (uint32_t)STAGE;                                                                \
+    } while (0)
+
+    while (c_ok) {
+        Item n_it;
+        const bool more = item_at(g, c_round + 1, n_it);
+        const int nstages = c_it.ke - c_it.kb;   // >= 1
+        for (int s = 0; s < nstages; s++) FP8K_STAGE();
+        st_cur += epilogue(c_it);
+#pragma unroll
+        for (int mi = 0; mi < 4; mi++)
+#pragma unroll
+            for (int nj = 0; nj < 2; nj++) acc[mi][nj] = vzero;
+        c_it = n_it;
+        c_ok = more;
+        c_round++;
+    }
+#undef FP8K_STAGE
+#undef FP8K_BLOCK_MI
+    wait_vm<0>();
+}
+
+}  // namespace blockw
+
+int gemm_block_wide_splits(int64_t I, int64_t J, int64_t K) {
+    const int64_t tiles = ((I + blockw::BM - 1) / blockw::BM) * ((J + blockw::BN - 1) / blockw::BN);
+    const int64_t kb = K / blockw::BK;
+    // aim for one work item per CU, keep >= 8 blocks of 128 per slice
+    int64_t s = 1;
+    while (tiles * s < 256 && kb / (s * 2) >= 8 && s < 64) s *= 2;
+    return (int)s;
+}
+
+hipError_t launch_gemm_block_wide(const GemmLaunch& l, int splits, hipStream_t stream) {
+    using namespace blockw;
+    Args g;
+    g.a = static_cast<const uint8_t*>(l.a);
+    g.b = static_cast<const uint8_t*>(l.b);
+    g.sa = l.sa;
+    g.sb = l.sb;
+    g.I = l.I;
+    g.J = l.J;
+    g.K = l.K;
+    g.c = static_cast<uint16_t*>(l.c);
+    g.part = static_cast<float*>(l.ws);
+    g.splits = splits;
+    g.tiles_i = (int)((l.I + BM - 1) / BM);
+    g.tiles_j = (int)((l.J + BN - 1) / BN);
+    g.ktiles = (int)(l.K / BK);
+    g.items = g.tiles_i * g.tiles_j * splits;
+    // raster groups as the tensorwise kernel (same tile)
+    g.gi = g.tiles_j >= 16 ? 8 : 2;
+    int grid = cu_count();
+    if (grid > g.items) grid = g.items;
+#define FP8K_LAUNCH(FA, FB) \
+    hipLaunchKernelGGL((gemm_block_wide_kernel<FA, FB>), dim3(grid), dim3(NW * 64), 0, stream, g)
+    if (l.fa == 0 && l.fb == 0) FP8K_LAUNCH(0, 0);
+    else if (l.fa == 1 && l.fb == 0) FP8K_LAUNCH(1, 0);
+    else if (l.fa == 0 && l.fb == 1) FP8K_LAUNCH(0, 1);
+    else FP8K_LAUNCH(1, 1);
+#undef FP8K_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace fp8k

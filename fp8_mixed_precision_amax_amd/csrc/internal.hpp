@@ -55,7 +55,9 @@ hipError_t launch_gemm_tensor(const GemmLaunch& l, int splits, hipStream_t strea
 // block-scaled kernel (gemm_block.hip)
 int gemm_block_splits(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm_block(const GemmLaunch& l, int splits, hipStream_t stream);
-int gemm_splits(int64_t I, int64_t J, int64_t K, bool block);
+// block-scaled kernel for B factors shared by 128-row groups (gemm_block_wide.hip)
+int gemm_block_wide_splits(int64_t I, int64_t J, int64_t K);
+hipError_t launch_gemm_block_wide(const GemmLaunch& l, int splits, hipStream_t stream);
 size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
 
