@@ -1,7 +1,9 @@
-// Block-scaled FP8 GEMM C[i][j] = sum_kb (sA[i][kb] sB[j][kb]) P_kb[i][j],
-// P_kb[i][j] = sum_{k in kb} A[i][k] B[j][k] over each 128-long contraction
-// block kb, on the gfx950 matrix cores (BF16 output, or fp32 partial sums for
-// split-K).
+// Block-scaled FP8 GEMM with per-row factors on both operands (1x128 x 1x128
+// blocks: the weight gradient of the Float8BlockScaling linear),
+// C[i][j] = sum_kb (sA[i][kb] sB[j][kb]) P_kb[i][j], P_kb[i][j] = sum_{k in kb}
+// A[i][k] B[j][k] over each 128-long contraction block kb, on the gfx950
+// matrix cores (BF16 output, or fp32 partial sums for split-K).  A B operand
+// with 128x128-block factors goes to gemm_block_wide.hip instead.
 //
 // Method: the Float8BlockScaling recipe (TransformerEngine issue 2852, the
 // question and its expected behaviour) quantizes activations and gradients in
@@ -24,9 +26,10 @@
 //    3 stages, 2 in flight.
 //  - promotion overlaps the matrix cores: the partial sums of blocks (0, *)
 //    are promoted right after the stage's last MFMAs issue, those of blocks
-//    (1, *) while the next stage's first MFMAs run; per-row B factors
-//    (1x128 x 1x128, the weight gradient) cost one multiply more per element
-//    than a factor shared by the tile (a 128x128 weight block).
+//    (1, *) while the next stage's first MFMAs run; every element is
+//    promoted with its own sA * sB (a multiply and an FMA).  A 256 x 256 tile
+//    (gemm_block_wide.hip's) measured no faster for this case: the two VALU
+//    operations per element, not the memory path, bound it.
 //  - stage hand-off and the inline-assembly LDS reads follow the tensorwise
 //    kernel: exact s_waitcnt vmcnt(n) on the wave's own DMA, then s_barrier;
 //    every read group is issued and waited for inside one asm statement.
@@ -171,30 +174,6 @@ __device__ __forceinline__ void read_half_sb_rows(v8i (&fa)[2], v8i (&fb)[2], f3
     sb[1][3] = g7;
 }
 
-// Second half with one B factor shared by the tile.
-__device__ __forceinline__ void read_half_sb_one(v8i (&fa)[2], v8i (&fb)[2], float& sb, uint32_t a0, uint32_t a1,
-                                                 uint32_t b0, uint32_t b1, uint32_t pb) {
-    u32x4 x0, x1, x2, x3, y0, y1, y2, y3;
-    asm volatile(
-        "ds_read_b128 %0, %9 offset:0\n\t"
-        "ds_read_b128 %1, %10 offset:0\n\t"
-        "ds_read_b128 %2, %9 offset:4096\n\t"
-        "ds_read_b128 %3, %10 offset:4096\n\t"
-        "ds_read_b128 %4, %11 offset:0\n\t"
-        "ds_read_b128 %5, %12 offset:0\n\t"
-        "ds_read_b128 %6, %11 offset:4096\n\t"
-        "ds_read_b128 %7, %12 offset:4096\n\t"
-        "ds_read_b32 %8, %13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(y0), "=&v"(y1), "=&v"(y2), "=&v"(y3), "=&v"(sb)
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(pb)
-        : "memory");
-    fa[0] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-    fa[1] = __builtin_bit_cast(v8i, __builtin_shufflevector(x2, x3, 0, 1, 2, 3, 4, 5, 6, 7));
-    fb[0] = __builtin_bit_cast(v8i, __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7));
-    fb[1] = __builtin_bit_cast(v8i, __builtin_shufflevector(y2, y3, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 // acc += P * (sa * sb[column]) for one 32 x 32 block
 __device__ __forceinline__ void promote_rows(v16f& acc, const v16f& p, float sa, const f32x4 (&sb)[4]) {
 #pragma unroll
@@ -205,12 +184,7 @@ __device__ __forceinline__ void promote_rows(v16f& acc, const v16f& p, float sa,
         acc[4 * q + 3] = __builtin_fmaf(p[4 * q + 3], sa * sb[q].w, acc[4 * q + 3]);
     }
 }
-__device__ __forceinline__ void promote_one(v16f& acc, const v16f& p, float t) {
-#pragma unroll
-    for (int v = 0; v < 16; v++) acc[v] = __builtin_fmaf(p[v], t, acc[v]);
-}
-
-template <int FA, int FB, bool SBROW>
+template <int FA, int FB>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
     // separate objects: the epilogue's LDS traffic never aliases the stages
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
@@ -306,7 +280,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
     const uint32_t offB = (uint32_t)(A_BYTES + brow * BK + ((ch ^ swz<BK>(brow)) << 4));
     const uint32_t offSA = (uint32_t)(SC_A + arow * 4);
     const uint32_t epi_slice = lds_off(sepi) + (uint32_t)(wave * SLICE);
-    const uint32_t offSB = SBROW ? (uint32_t)(SC_B + (wj * 64 + 4 * (lane >> 5)) * 4) : (uint32_t)(SC_B + wj * 64 * 4);
+    const uint32_t offSB = (uint32_t)(SC_B + (wj * 64 + 4 * (lane >> 5)) * 4);
 
     v16f acc[2][2], p[2][2];
 #pragma unroll
@@ -322,7 +296,6 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
     // factors of the stage whose blocks (1, *) still wait for promotion
     float sa1_prev = 0.0f;
     f32x4 sbr_prev[2][4];
-    float sb1_prev = 0.0f;
 #pragma unroll
     for (int nj = 0; nj < 2; nj++)
 #pragma unroll
@@ -334,10 +307,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
     // the epilogue stores since), then the barrier, which also retires every
     // wave's reads of the buffer the DMA below overwrites (all LDS reads are
     // waited for inside their asm statements).
-#define FP8K_PROMOTE(MI, NJ, SA, SBR, SB1)                                  \
+#define FP8K_PROMOTE(MI, NJ, SA, SBR)                                  \
     do {                                                                    \
-        if constexpr (SBROW) promote_rows(acc[MI][NJ], p[MI][NJ], SA, SBR[NJ]); \
-        else promote_one(acc[MI][NJ], p[MI][NJ], (SA) * (SB1));             \
+        promote_rows(acc[MI][NJ], p[MI][NJ], SA, SBR[NJ]);                  \
     } while (0)
 #define FP8K_STEP(DEFER)                                                                           \
     do {                                                                                           \
@@ -354,34 +326,31 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
         __builtin_amdgcn_sched_barrier(0);                                                         \
         /* each promotion issues behind one MFMA (MFMA first) */                                   \
         p[0][0] = mfma<FA, FB>(fb_[0], fa_[0], vzero);                                             \
-        if (DEFER) FP8K_PROMOTE(1, 0, sa1_prev, sbr_prev, sb1_prev);                               \
+        if (DEFER) FP8K_PROMOTE(1, 0, sa1_prev, sbr_prev);                               \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
         __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         p[0][1] = mfma<FA, FB>(fb_[1], fa_[0], vzero);                                             \
-        if (DEFER) FP8K_PROMOTE(1, 1, sa1_prev, sbr_prev, sb1_prev);                               \
+        if (DEFER) FP8K_PROMOTE(1, 1, sa1_prev, sbr_prev);                               \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
         __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         p[1][0] = mfma<FA, FB>(fb_[0], fa_[1], vzero);                                             \
         p[1][1] = mfma<FA, FB>(fb_[1], fa_[1], vzero);                                             \
         __builtin_amdgcn_sched_barrier(0);                                                         \
-        if constexpr (SBROW)                                                                       \
-            read_half_sb_rows(fa_, fb_, sbr_prev, a0_ ^ 64u, a1_ ^ 64u, b0_ ^ 64u, b1_ ^ 64u, sb_ + offSB); \
-        else                                                                                       \
-            read_half_sb_one(fa_, fb_, sb1_prev, a0_ ^ 64u, a1_ ^ 64u, b0_ ^ 64u, b1_ ^ 64u, sb_ + offSB); \
+        read_half_sb_rows(fa_, fb_, sbr_prev, a0_ ^ 64u, a1_ ^ 64u, b0_ ^ 64u, b1_ ^ 64u, sb_ + offSB);    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         p[0][0] = mfma<FA, FB>(fb_[0], fa_[0], p[0][0]);                                           \
         p[0][1] = mfma<FA, FB>(fb_[1], fa_[0], p[0][1]);                                           \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         /* blocks (0, *) completed two MFMAs earlier */                                            \
         p[1][0] = mfma<FA, FB>(fb_[0], fa_[1], p[1][0]);                                           \
-        FP8K_PROMOTE(0, 0, sa0_, sbr_prev, sb1_prev);                                              \
+        FP8K_PROMOTE(0, 0, sa0_, sbr_prev);                                              \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
         __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         p[1][1] = mfma<FA, FB>(fb_[1], fa_[1], p[1][1]);                                           \
-        FP8K_PROMOTE(0, 1, sa0_, sbr_prev, sb1_prev);                                              \
+        FP8K_PROMOTE(0, 1, sa0_, sbr_prev);                                              \
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
         __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                         \
@@ -459,8 +428,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
         FP8K_STEP(false);
         for (int s = 1; s < nsteps; s++) FP8K_STEP(true);
         // the item's last blocks (1, *), then its output
-        FP8K_PROMOTE(1, 0, sa1_prev, sbr_prev, sb1_prev);
-        FP8K_PROMOTE(1, 1, sa1_prev, sbr_prev, sb1_prev);
+        FP8K_PROMOTE(1, 0, sa1_prev, sbr_prev);
+        FP8K_PROMOTE(1, 1, sa1_prev, sbr_prev);
         st_cur += epilogue(c_it);
 #pragma unroll
         for (int mi = 0; mi < 2; mi++)
@@ -510,12 +479,8 @@ hipError_t launch_gemm_block(const GemmLaunch& l, int splits, hipStream_t stream
     g.gi = 8;
     int grid = cu_count();
     if (grid > g.items) grid = g.items;
-    const bool sbrow = l.sb.group == 1;
-#define FP8K_LAUNCH(FA, FB)                                                                                  \
-    do {                                                                                                     \
-        if (sbrow) hipLaunchKernelGGL((gemm_block_kernel<FA, FB, true>), dim3(grid), dim3(NW * 64), 0, stream, g); \
-        else hipLaunchKernelGGL((gemm_block_kernel<FA, FB, false>), dim3(grid), dim3(NW * 64), 0, stream, g);      \
-    } while (0)
+#define FP8K_LAUNCH(FA, FB) \
+    hipLaunchKernelGGL((gemm_block_kernel<FA, FB>), dim3(grid), dim3(NW * 64), 0, stream, g)
     if (l.fa == 0 && l.fb == 0) FP8K_LAUNCH(0, 0);
     else if (l.fa == 1 && l.fb == 0) FP8K_LAUNCH(1, 0);
     else if (l.fa == 0 && l.fb == 1) FP8K_LAUNCH(0, 1);
