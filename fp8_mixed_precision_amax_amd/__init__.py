@@ -18,7 +18,8 @@ from ._lib import (E4M3, E5M2, LAYOUT_COL, LAYOUT_ROW, RECIPE_BLOCK, RECIPE_TENS
 
 __all__ = ["block_gemm_scale", "E4M3", "E5M2", "SCALE_TENSOR", "SCALE_1x128", "SCALE_128x128", "RECIPE_TENSOR",
            "RECIPE_BLOCK", "LAYOUT_ROW", "LAYOUT_COL", "Fp8Error", "QTensor", "quantize",
-           "gemm", "WeightCache", "Fp8Linear", "linear_workspace", "lib"]
+           "gemm", "WeightCache", "Fp8Linear", "linear_workspace", "lib", "amax_partials",
+           "AMAX_PARTIALS_BYTES"]
 
 
 def lib():
@@ -77,8 +78,19 @@ class QTensor:
                                 self.scale_col, self.scale_inv_col, self.amax)))
 
 
-def quantize(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None):
-    """Current-scaling FP8 quantization of a bf16 [rows, cols] device tensor."""
+AMAX_PARTIALS_BYTES = 4096   # FP8_AMAX_PARTIALS_BYTES
+
+
+def amax_partials(device):
+    """Device buffer for the amax hand-off (2048 16-bit partial maxima)."""
+    return torch.empty(AMAX_PARTIALS_BYTES, dtype=torch.uint8, device=device)
+
+
+def quantize(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None,
+             amax_partials=None):
+    """Current-scaling FP8 quantization of a bf16 [rows, cols] device tensor.
+    amax_partials (tensorwise only): x's amax partials from its producer
+    (fp8_quantize_from_amax: the cast pass alone)."""
     L = lib()
     if x.dtype != torch.bfloat16 or x.dim() != 2:
         raise ValueError("x must be a 2-D bfloat16 tensor")
@@ -86,6 +98,13 @@ def quantize(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=
     R, C = x.shape
     if out is None:
         out = QTensor(R, C, scaling, _dev(x), row=bool(layouts & LAYOUT_ROW), col=bool(layouts & LAYOUT_COL))
+    if amax_partials is not None:
+        if scaling != SCALE_TENSOR:
+            raise ValueError("amax partials serve the tensorwise quantize")
+        oc = out.c()
+        _lib.check(L.fp8_quantize_from_amax(_ptr(x), R, C, fmt, layouts, ctypes.byref(oc), _ptr(amax_partials),
+                                            _stream(stream)))
+        return out
     wsb = L.fp8_quantize_workspace_bytes(R, C, scaling)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
     oc = out.c()
@@ -109,9 +128,10 @@ def block_gemm_scale(sinv, group):
     return gemm_scale(sinv, group, sinv.stride(0), sinv.stride(1))
 
 
-def gemm(a, fa, sa, b, fb, sb, out=None, stream=None):
+def gemm(a, fa, sa, b, fb, sb, out=None, stream=None, amax_out=None):
     """C[i][j] = bf16(sum_k A[i][k] B[j][k] * scales); a [I, K], b [J, K]
-    uint8 FP8 codes; sa / sb are GemmScaleC (see gemm_scale)."""
+    uint8 FP8 codes; sa / sb are GemmScaleC (see gemm_scale).  amax_out
+    (tensorwise only): receives C's amax partials (fp8_gemm_amax)."""
     L = lib()
     I, K = a.shape
     J, K2 = b.shape
@@ -121,8 +141,12 @@ def gemm(a, fa, sa, b, fb, sb, out=None, stream=None):
         out = torch.empty((I, J), dtype=torch.bfloat16, device=a.device)
     wsb = L.fp8_gemm_workspace_bytes(I, J, K)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=a.device)
-    _lib.check(L.fp8_gemm(_ptr(a), fa, sa, _ptr(b), fb, sb, I, J, K, _ptr(out), _ptr(ws), wsb,
-                          _stream(stream)))
+    if amax_out is not None:
+        _lib.check(L.fp8_gemm_amax(_ptr(a), fa, sa, _ptr(b), fb, sb, I, J, K, _ptr(out), _ptr(amax_out), _ptr(ws),
+                                   wsb, _stream(stream)))
+    else:
+        _lib.check(L.fp8_gemm(_ptr(a), fa, sa, _ptr(b), fb, sb, I, J, K, _ptr(out), _ptr(ws), wsb,
+                              _stream(stream)))
     return out
 
 
@@ -180,18 +204,24 @@ class Fp8Linear:
         self.ws, self.ws_bytes = linear_workspace(N, K, M, recipe, device)
         self._sx, self._dq, self._wq = self.saved_x.c(), self.dy_q.c(), self.w_q.c()
 
-    def forward(self, x, w, y=None, is_first_microbatch=None, stream=None):
+    def forward(self, x, w, y=None, is_first_microbatch=None, stream=None, x_amax=None, y_amax=None):
+        """x_amax: X's amax partials from its producer (skips X's amax pass);
+        y_amax: receives Y's partials (tensorwise recipe)."""
         flag = -1 if is_first_microbatch is None else int(bool(is_first_microbatch))
         if y is None:
             y = torch.empty((self.N, self.M), dtype=torch.bfloat16, device=x.device)
         cache = self.cache.handle if (self.cache is not None and flag != -1) else None
         _lib.check(lib().fp8_linear_fwd(_ptr(x), _ptr(w), self.N, self.K, self.M, self.recipe, cache, flag,
                                         _ptr(y), ctypes.byref(self._sx), ctypes.byref(self._wq),
-                                        _ptr(self.ws), self.ws_bytes, _stream(stream)))
+                                        _ptr(x_amax), _ptr(y_amax), _ptr(self.ws), self.ws_bytes,
+                                        _stream(stream)))
         self._last_flag = flag
         return y
 
-    def backward(self, dy, dx=None, dw=None, need_dx=True, need_dw=True, stream=None):
+    def backward(self, dy, dx=None, dw=None, need_dx=True, need_dw=True, stream=None, dy_amax=None,
+                 dx_amax=None):
+        """dy_amax: dY's amax partials from its producer (skips dY's amax
+        pass); dx_amax: receives dX's partials (tensorwise recipe)."""
         if need_dx and dx is None:
             dx = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dy.device)
         if need_dw and dw is None:
@@ -201,7 +231,8 @@ class Fp8Linear:
                                         ctypes.byref(self._sx), self.cache.handle if use_cache else None,
                                         ctypes.byref(self._wq), ctypes.byref(self._dq),
                                         _ptr(dx) if need_dx else None, _ptr(dw) if need_dw else None,
-                                        _ptr(self.ws), self.ws_bytes, _stream(stream)))
+                                        _ptr(dy_amax), _ptr(dx_amax), _ptr(self.ws), self.ws_bytes,
+                                        _stream(stream)))
         return dx, dw
 
     def weight_q(self):

@@ -107,8 +107,10 @@ fp8_status hip_status(hipError_t e, const char* what) {
     return FP8_OK;
 }
 
+// given_amax: tensorwise only, the amax partials of x from its producer (the
+// amax pass is skipped); otherwise ws holds the pass's partials
 fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, int scaling, unsigned layouts,
-                       const fp8_qtensor* out, void* ws, hipStream_t st) {
+                       const fp8_qtensor* out, void* ws, hipStream_t st, const void* given_amax = nullptr) {
     fp8k::QuantizeLaunch q;
     q.x = x;
     q.rows = rows;
@@ -122,7 +124,8 @@ fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, in
     q.scale_col = out->scale_col;
     q.scale_inv_col = out->scale_inv_col;
     q.amax = scaling == FP8_SCALE_TENSOR ? out->amax : nullptr;
-    q.partial = static_cast<uint16_t*>(ws);
+    q.partial = given_amax ? static_cast<uint16_t*>(const_cast<void*>(given_amax)) : static_cast<uint16_t*>(ws);
+    q.partial_given = given_amax != nullptr;
     return hip_status(fp8k::launch_quantize(q, st), "quantize launch");
 }
 
@@ -135,7 +138,8 @@ fp8k::GemmScale block_scale(const float* sinv, int64_t group, int64_t sr, int64_
 constexpr int64_t kMaxContraction = int64_t(1) << 23;
 
 fp8_status do_gemm(const void* a, int fa, fp8k::GemmScale sa, const void* b, int fb, fp8k::GemmScale sb, int64_t I,
-                   int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, hipStream_t st) {
+                   int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, hipStream_t st,
+                   void* c_amax = nullptr) {
     if (K >= kMaxContraction)
         return fail(FP8_ERR_SHAPE, "contraction length %lld: must be below 2^23", (long long)K);
     fp8k::GemmLaunch g;
@@ -151,6 +155,7 @@ fp8_status do_gemm(const void* a, int fa, fp8k::GemmScale sa, const void* b, int
     g.c = c;
     g.ws = ws;
     g.ws_bytes = ws_bytes;
+    g.c_amax = static_cast<uint16_t*>(c_amax);
     return hip_status(fp8k::launch_gemm(g, st), "gemm launch");
 }
 
@@ -213,10 +218,19 @@ fp8_status fp8_quantize(const void* x, int64_t rows, int64_t cols, fp8_format fo
     return do_quantize(x, rows, cols, format, scaling, layouts, out, ws, static_cast<hipStream_t>(stream));
 }
 
+fp8_status fp8_quantize_from_amax(const void* x, int64_t rows, int64_t cols, fp8_format format, unsigned layouts,
+                                  const fp8_qtensor* out, const void* amax_partials, void* stream) {
+    FP8_TRY(check_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out));
+    FP8_TRY(check_ptr16("amax_partials", amax_partials));
+    return do_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out, nullptr, static_cast<hipStream_t>(stream),
+                       amax_partials);
+}
+
 size_t fp8_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K) { return fp8k::gemm_ws_bytes(I, J, K); }
 
-fp8_status fp8_gemm(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb, fp8_gemm_scale sb,
-                    int64_t I, int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, void* stream) {
+static fp8_status gemm_checked(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb,
+                               fp8_gemm_scale sb, int64_t I, int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes,
+                               void* stream, void* c_amax) {
     FP8_TRY(check_dims("gemm I x J", I, J));
     FP8_TRY(check_dims("gemm K", K, 128));
     if (K >= kMaxContraction) return fail(FP8_ERR_SHAPE, "contraction length %lld: must be below 2^23", (long long)K);
@@ -236,9 +250,25 @@ fp8_status fp8_gemm(const void* a, fp8_format fa, fp8_gemm_scale sa, const void*
         if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
         FP8_TRY(check_ptr16("ws", ws));
     }
+    if (c_amax) {
+        if (sa.group != 0) return fail(FP8_ERR_ENUM, "the output amax hand-off is for tensorwise GEMMs");
+        FP8_TRY(check_ptr16("c_amax_partials", c_amax));
+    }
     return do_gemm(a, fa, fp8k::GemmScale{sa.scale_inv, sa.group, sa.stride_r, sa.stride_kb}, b, fb,
                    fp8k::GemmScale{sb.scale_inv, sb.group, sb.stride_r, sb.stride_kb}, I, J, K, c, ws, ws_bytes,
-                   static_cast<hipStream_t>(stream));
+                   static_cast<hipStream_t>(stream), c_amax);
+}
+
+fp8_status fp8_gemm(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb, fp8_gemm_scale sb,
+                    int64_t I, int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, void* stream) {
+    return gemm_checked(a, fa, sa, b, fb, sb, I, J, K, c, ws, ws_bytes, stream, nullptr);
+}
+
+fp8_status fp8_gemm_amax(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb,
+                         fp8_gemm_scale sb, int64_t I, int64_t J, int64_t K, void* c, void* c_amax_partials, void* ws,
+                         size_t ws_bytes, void* stream) {
+    if (!c_amax_partials) return fail(FP8_ERR_NULL, "c_amax_partials is NULL");
+    return gemm_checked(a, fa, sa, b, fb, sb, I, J, K, c, ws, ws_bytes, stream, c_amax_partials);
 }
 
 fp8_status fp8_wcache_create(int64_t M, int64_t K, fp8_recipe recipe, const fp8_qtensor* bufs, fp8_wcache* out) {
@@ -294,13 +324,25 @@ static fp8_status check_cache(fp8_wcache cache, int64_t M, int64_t K, int recipe
     return FP8_OK;
 }
 
+// The optional amax hand-off buffers of the linear (tensorwise recipe only).
+static fp8_status check_amax_handoff(int recipe, const void* in, const void* out, const char* in_name,
+                                     const char* out_name) {
+    if (!in && !out) return FP8_OK;
+    if (recipe != FP8_RECIPE_TENSOR) return fail(FP8_ERR_ENUM, "the amax hand-off is for the tensorwise recipe");
+    if (in) FP8_TRY(check_ptr16(in_name, in));
+    if (out) FP8_TRY(check_ptr16(out_name, out));
+    return FP8_OK;
+}
+
 fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
                           fp8_wcache cache, int flag, void* y, const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
-                          void* ws, size_t ws_bytes, void* stream) {
+                          const void* x_amax_partials, void* y_amax_partials, void* ws, size_t ws_bytes,
+                          void* stream) {
     FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes));
     if (flag != -1 && flag != 0 && flag != 1) return fail(FP8_ERR_ENUM, "is_first_microbatch must be -1, 0 or 1");
     FP8_TRY(check_ptr16("x", x));
     FP8_TRY(check_ptr16("y", y));
+    FP8_TRY(check_amax_handoff(recipe, x_amax_partials, y_amax_partials, "x_amax_partials", "y_amax_partials"));
     const int act = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
     const int wsc = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_128x128 : FP8_SCALE_TENSOR;
     FP8_TRY(check_quantize(x, N, K, FP8_E4M3, act, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x));
@@ -329,20 +371,23 @@ fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, in
             cache->fills++;
         }
     }
-    FP8_TRY(do_quantize(x, N, K, FP8_E4M3, act, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x, ws, st));
+    FP8_TRY(do_quantize(x, N, K, FP8_E4M3, act, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x, ws, st, x_amax_partials));
     if (recipe == FP8_RECIPE_TENSOR)
         return do_gemm(saved_x->q_row, FP8_E4M3, tensor_scale(saved_x->scale_inv), wq->q_row, FP8_E4M3,
-                       tensor_scale(wq->scale_inv), N, M, K, y, gws, gws_bytes, st);
+                       tensor_scale(wq->scale_inv), N, M, K, y, gws, gws_bytes, st, y_amax_partials);
     return do_gemm(saved_x->q_row, FP8_E4M3, block_scale(saved_x->scale_inv, 1, 1, N), wq->q_row, FP8_E4M3,
                    block_scale(wq->scale_inv, 128, K / 128, 1), N, M, K, y, gws, gws_bytes, st);
 }
 
 fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
                           const fp8_qtensor* saved_x, fp8_wcache cache, const fp8_qtensor* w_q,
-                          const fp8_qtensor* dy_q, void* dx, void* dw, void* ws, size_t ws_bytes, void* stream) {
+                          const fp8_qtensor* dy_q, void* dx, void* dw, const void* dy_amax_partials,
+                          void* dx_amax_partials, void* ws, size_t ws_bytes, void* stream) {
     FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes));
     FP8_TRY(check_ptr16("dy", dy));
     if (!dx && !dw) return fail(FP8_ERR_NULL, "both dx and dw are NULL: nothing to compute");
+    FP8_TRY(check_amax_handoff(recipe, dy_amax_partials, dx_amax_partials, "dy_amax_partials", "dx_amax_partials"));
+    if (dx_amax_partials && !dx) return fail(FP8_ERR_NULL, "dx_amax_partials given without dx");
     if (dx) FP8_TRY(check_ptr16("dx", dx));
     if (dw) FP8_TRY(check_ptr16("dw", dw));
     const int act = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
@@ -369,11 +414,11 @@ fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_r
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     void* gws = wsb + kPartialBytes;
     const size_t gws_bytes = ws_bytes - kPartialBytes;
-    FP8_TRY(do_quantize(dy, N, M, FP8_E5M2, act, lay, dy_q, ws, st));
+    FP8_TRY(do_quantize(dy, N, M, FP8_E5M2, act, lay, dy_q, ws, st, dy_amax_partials));
     if (dx) {
         if (recipe == FP8_RECIPE_TENSOR)
             FP8_TRY(do_gemm(dy_q->q_row, FP8_E5M2, tensor_scale(dy_q->scale_inv), wq->q_col, FP8_E4M3,
-                            tensor_scale(wq->scale_inv), N, K, M, dx, gws, gws_bytes, st));
+                            tensor_scale(wq->scale_inv), N, K, M, dx, gws, gws_bytes, st, dx_amax_partials));
         else
             FP8_TRY(do_gemm(dy_q->q_row, FP8_E5M2, block_scale(dy_q->scale_inv, 1, 1, N), wq->q_col, FP8_E4M3,
                             block_scale(wq->scale_inv, 128, 1, K / 128), N, K, M, dx, gws, gws_bytes, st));

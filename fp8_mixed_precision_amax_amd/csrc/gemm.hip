@@ -8,16 +8,21 @@
 // slice writes fp32 partials; the reduce kernel sums the slices in fixed
 // order, applies the tensorwise factor (block-scaled partials already carry
 // theirs) and rounds to bf16.
+#include "device.hpp"
 #include "gemm_common.hpp"
 #include "internal.hpp"
 
 namespace fp8k {
 
 // Sum split-K partials in split order, apply the tensorwise factor, bf16.
+// With amax_part, also one partial max |bf16 C| per block (block 0 zeroes the
+// slots no block owns).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t n4,
                                                             int64_t IJ, const float* sa, const float* sb,
-                                                            int tensorwise, uint16_t* __restrict__ c) {
+                                                            int tensorwise, uint16_t* __restrict__ c,
+                                                            uint16_t* __restrict__ amax_part) {
     const float t = tensorwise ? sa[0] * sb[0] : 1.0f;
+    uint32_t amx = 0;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
         float4 s = reinterpret_cast<const float4*>(part)[i];
         for (int z = 1; z < splits; z++) {
@@ -30,6 +35,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
         reinterpret_cast<uint2*>(c)[i] = w;
+        amx = pkmax_u16(amx, pkmax_u16(mag2(w.x), mag2(w.y)));
+    }
+    if (amax_part) {
+        __shared__ uint32_t red[4];
+        const uint32_t m = wave_max_u32(hmax_u16(amx));
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t r = red[0];
+            for (int w = 1; w < 4; w++) r = r > red[w] ? r : red[w];
+            amax_part[blockIdx.x] = (uint16_t)r;
+        }
+        if (blockIdx.x == 0)
+            for (int p = (int)gridDim.x + (int)threadIdx.x; p < kMaxAmaxPartials; p += 256) amax_part[p] = 0;
     }
 }
 
@@ -72,10 +91,10 @@ hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream) {
     if (e != hipSuccess || splits == 1) return e;
     const int64_t n4 = l.I * l.J / 4;
     int64_t blocks = (n4 + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > kMaxAmaxPartials) blocks = kMaxAmaxPartials;   // one amax partial per block
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const float*>(l.ws), splits, n4, l.I * l.J, l.sa.sinv, l.sb.sinv, block ? 0 : 1,
-                       static_cast<uint16_t*>(l.c));
+                       static_cast<uint16_t*>(l.c), block ? nullptr : l.c_amax);
     return hipGetLastError();
 }
 

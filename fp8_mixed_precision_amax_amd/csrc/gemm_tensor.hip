@@ -40,6 +40,7 @@
 //  - epilogue: each wave converts 32 rows at a time to bf16 into a private
 //    4 KiB LDS slice (chunk-major, (row ^ 2 chunk) swizzle: conflict-free
 //    writes and reads) and stores whole 128-byte row segments.
+#include "device.hpp"
 #include "gemm_common.hpp"
 #include "internal.hpp"
 
@@ -72,6 +73,7 @@ struct Args {
     float* part;          // split-K partials [splits][I][J]
     int splits, tiles_i, tiles_j, kpairs, items;   // kpairs: contraction blocks of 128
     int gi;               // tile rows per raster group
+    uint16_t* amax_part;  // optional: one partial max |bf16 C| per workgroup, zeros after
 };
 
 struct Item {
@@ -223,6 +225,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     const uint32_t rc = (uint32_t)(lane & 7), rr = (uint32_t)(lane >> 3);
     const uint32_t goff = (uint32_t)(rr * (uint32_t)g.J * 2 + rc * 16);
 
+    // max |bf16| of the outputs this lane wrote (two packed 16-bit
+    // magnitudes; NaN magnitudes exceed +Inf's, so NaN propagates)
+    uint32_t amx = 0;
+
     // write one item's accumulators; returns the vector-memory stores issued
     auto epilogue = [&](const Item& it) __attribute__((always_inline)) -> int {
         const int64_t i0 = (int64_t)it.ti * BM, j0 = (int64_t)it.tj * BN;
@@ -256,6 +262,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
                     uint2 w;
                     w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
                     w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                    amx = pkmax_u16(amx, pkmax_u16(mag2(w.x), mag2(w.y)));
                     const int chunk = nj * 4 + q;
                     const uint32_t wa = wbase + (uint32_t)(chunk * 512 + ((frow ^ (2 * chunk)) << 4));
                     asm volatile("ds_write_b64 %0, %1" : : "v"(wa), "v"(w) : "memory");
@@ -367,6 +374,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
                  : "memory");
     if (have_prev) epilogue(p_it);
     wait_vm<0>();
+    if (g.amax_part) {
+        // workgroup max through the (now idle) epilogue slices, one partial
+        // per workgroup; workgroup 0 zeroes the slots no workgroup owns
+        const uint32_t m = wave_max_u32(hmax_u16(amx));
+        uint32_t* red = reinterpret_cast<uint32_t*>(sepi);
+        __syncthreads();
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t r = red[0];
+#pragma unroll
+            for (int w = 1; w < NW; w++) r = r > red[w] ? r : red[w];
+            g.amax_part[blockIdx.x] = (uint16_t)r;
+        }
+        if (blockIdx.x == 0)
+            for (int p = (int)gridDim.x + (int)threadIdx.x; p < kMaxAmaxPartials; p += NW * 64) g.amax_part[p] = 0;
+    }
 }
 
 }  // namespace tensor
@@ -398,6 +422,8 @@ hipError_t launch_gemm_tensor(const GemmLaunch& l, int splits, hipStream_t strea
     g.tiles_j = (int)((l.J + BN - 1) / BN);
     g.kpairs = (int)(l.K / 128);
     g.items = g.tiles_i * g.tiles_j * splits;
+    // the split-K reduce emits the amax of a split output
+    g.amax_part = splits == 1 ? l.c_amax : nullptr;
     // an XCD's 32 concurrent items cover 8 tile rows x 4 columns when the
     // output is wide (8192 x 8192 x 16384: 955 -> 820 us against groups of
     // 2), 16 x 2 when it has few tile columns (131072 x 512 x 2048: 139 us

@@ -22,6 +22,8 @@ struct QuantizeLaunch {
     float* scale_inv_col;
     float* amax;        // optional
     uint16_t* partial;  // tensor: kMaxAmaxPartials 16-bit slots of scratch (16-byte aligned)
+    bool partial_given; // tensor: partial already holds the amax partials of x (written by
+                        // the producer of x); the amax pass is skipped
 };
 
 int amax_partial_count(int64_t numel);
@@ -45,6 +47,8 @@ struct GemmLaunch {
     void* c;            // [I, J] bf16
     void* ws;           // split-K partials
     size_t ws_bytes;
+    uint16_t* c_amax;   // tensorwise, optional: kMaxAmaxPartials partial maxima of |C|
+                        // (bf16 magnitude bits, 0 in unused slots)
 };
 
 // Split-K factor the GEMM launcher will use for this shape (1 = none) and

@@ -300,7 +300,7 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     a.scale_inv_col = q.scale_inv_col;
     a.amax_out = q.amax;
     a.partial = q.partial;
-    if (q.scaling == 0) {
+    if (q.scaling == 0 && !q.partial_given) {
         const int g = amax_partial_count(q.rows * q.cols);
         hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(kAmaxThreads), 0, stream,
                            static_cast<const uint4*>(q.x), q.rows * q.cols / 8, q.partial);

@@ -145,6 +145,36 @@ fp8_status fp8_quantize(const void* x_bf16, int64_t rows, int64_t cols,
                         const fp8_qtensor* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Amax hand-off (producer-side amax).  The tensorwise quantize of x needs
+ * amax(x) before it can encode, so by itself it reads x twice (the amax pass,
+ * then the cast); the quantization reductions are the non-GEMM work of an FP8
+ * linear ("Native FP8 MLP reconstruction", discussion: the model's FLOP
+ * estimate leaves them out with the casts and layout writes).  When x is the
+ * bf16 output of a GEMM of this library, that GEMM can emit the amax as it
+ * writes x, and the quantize then reads x once:
+ *   amax partials  FP8_AMAX_PARTIALS_BYTES of device memory (16-byte aligned):
+ *                  2048 16-bit slots, each the maximum bf16 magnitude bits
+ *                  (|x| as a bf16 bit pattern, NaN above +Inf) over a part of
+ *                  x, unused slots 0.  amax(x) = the maximum over the slots.
+ * Written by fp8_gemm_amax (and the linear entry points' *_amax_partials
+ * outputs), read by fp8_quantize_from_amax (and their *_amax_partials
+ * inputs).  The quantized bytes and scales are identical to fp8_quantize's
+ * on the same x.
+ */
+#define FP8_AMAX_PARTIALS_BYTES 4096
+
+/*
+ * Tensorwise quantize of x whose amax partials were written by the producer
+ * of x (see above): the cast pass alone, no workspace.  Arguments and outputs
+ * as fp8_quantize with scaling = FP8_SCALE_TENSOR; amax_partials must be
+ * non-NULL and 16-byte aligned.  Results are undefined if the partials do not
+ * describe x.
+ */
+fp8_status fp8_quantize_from_amax(const void* x_bf16, int64_t rows, int64_t cols, fp8_format format,
+                                  unsigned layouts, const fp8_qtensor* out, const void* amax_partials,
+                                  void* stream);
+
+/*
  * Scale of an FP8 GEMM operand (dequantisation factors):
  *   group == 0:  tensorwise, the factor is scale_inv[0]
  *   group >= 1:  the factor of operand row r in contraction block kb
@@ -181,6 +211,17 @@ fp8_status fp8_gemm(const void* a, fp8_format format_a, fp8_gemm_scale scale_a,
                     int64_t I, int64_t J, int64_t K, void* c_bf16,
                     void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * fp8_gemm (tensorwise operands only: FP8_ERR_ENUM otherwise) that also
+ * writes the amax partials of its bf16 output C into c_amax_partials (see
+ * "Amax hand-off"; NULL is FP8_ERR_NULL).  C is bitwise the same as
+ * fp8_gemm's.
+ */
+fp8_status fp8_gemm_amax(const void* a, fp8_format format_a, fp8_gemm_scale scale_a,
+                         const void* b, fp8_format format_b, fp8_gemm_scale scale_b,
+                         int64_t I, int64_t J, int64_t K, void* c_bf16, void* c_amax_partials,
+                         void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------- weight cache --------------------------- */
 
 /*
@@ -216,11 +257,16 @@ size_t fp8_linear_workspace_bytes(int64_t N, int64_t K, int64_t M, fp8_recipe re
  *                read (it may be NULL); FP8_ERR_CACHE_EMPTY if the cache was
  *                never filled.
  *   A cache whose M, K or recipe differ gives FP8_ERR_CACHE_MISMATCH.
+ *   Amax hand-off (tensorwise recipe only, FP8_ERR_ENUM otherwise; each may
+ *   be NULL): x_amax_partials, written by the producer of X (the previous
+ *   layer's forward), replaces X's amax pass; y_amax_partials receives Y's
+ *   partials for the next layer.
  */
 fp8_status fp8_linear_fwd(const void* x_bf16, const void* w_bf16,
                           int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
                           fp8_wcache cache, int is_first_microbatch,
                           void* y_bf16, const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
+                          const void* x_amax_partials, void* y_amax_partials,
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -229,10 +275,14 @@ fp8_status fp8_linear_fwd(const void* x_bf16, const void* w_bf16,
  * dW [M, K] = dY^T X (E5M2 x E4M3, both col layouts).  The weight comes from
  * the cache when cache != NULL (it must be valid), else from w_q as written
  * by fp8_linear_fwd.  dx_bf16 or dw_bf16 may be NULL to skip that GEMM.
+ * Amax hand-off (tensorwise recipe only; each may be NULL): dy_amax_partials,
+ * written by the producer of dY (the next layer's backward), replaces dY's
+ * amax pass; dx_amax_partials receives dX's partials (dx_bf16 must be given).
  */
 fp8_status fp8_linear_bwd(const void* dy_bf16, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
                           const fp8_qtensor* saved_x, fp8_wcache cache, const fp8_qtensor* w_q,
                           const fp8_qtensor* dy_q, void* dx_bf16, void* dw_bf16,
+                          const void* dy_amax_partials, void* dx_amax_partials,
                           void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------- misc -------------------------------- */

@@ -75,6 +75,10 @@ def test_quantize_argument_errors(L):
     assert quant(L, wsb=100) == WORKSPACE
     assert quant(L, ws=None) == NULL
     assert L.fp8_quantize(A, 256, 256, 0, 0, 3, None, A, 4096, None) == NULL
+    # the cast-only variant: partials required and 16-byte aligned
+    assert L.fp8_quantize_from_amax(A, 256, 256, 0, 3, ctypes.byref(qt()), None, None) == NULL
+    assert L.fp8_quantize_from_amax(A, 256, 256, 0, 3, ctypes.byref(qt()), U, None) == ALIGN
+    assert L.fp8_quantize_from_amax(A, 200, 256, 0, 3, ctypes.byref(qt()), A, None) == SHAPE
 
 
 def test_last_error_message(L):
@@ -111,6 +115,12 @@ def test_gemm_argument_errors(L):
     # before the workspace
     assert g(K=1 << 23, wsb=0) == SHAPE
     assert g(K=(1 << 23) - 128, wsb=0) == WORKSPACE
+    # the output-amax variant: tensorwise only, the partials buffer required
+    def ga(c_amax=A, sa=None, sb=None):
+        return L.fp8_gemm_amax(A, 0, sa or gs(), A, 0, sb or gs(), 256, 256, 256, A, c_amax, A, 1 << 30, None)
+    assert ga(c_amax=None) == NULL
+    assert ga(c_amax=U) == ALIGN
+    assert ga(sa=gs(group=1, sr=1, sk=256), sb=gs(group=1, sr=1, sk=256)) == ENUM
 
 
 def make_cache(L, M=256, K=256, recipe=0, bufs=None):
@@ -133,32 +143,36 @@ def test_cache_lifecycle_and_errors(L):
     N, K, M = 256, 256, 256
     wsb = L.fp8_linear_workspace_bytes(N, K, M, 0)
     sx = qt()
+
+    def fwd(x, w, N, K, M, recipe, cache, flag, wq, ws, wsb_, xa=None, ya=None):
+        return L.fp8_linear_fwd(x, w, N, K, M, recipe, cache, flag, A, ctypes.byref(sx), wq, xa, ya, ws, wsb_, None)
+
+    def bwd(N, K, M, recipe, cache, wq, dq, dx, dw, ws, wsb_, dya=None, dxa=None):
+        return L.fp8_linear_bwd(A, N, K, M, recipe, ctypes.byref(sx), cache, wq, dq, dx, dw, dya, dxa, ws, wsb_, None)
+
     # False on an empty cache
-    r = L.fp8_linear_fwd(A, None, N, K, M, 0, h, 0, A, ctypes.byref(sx), None, A, wsb, None)
-    assert r == CACHE_EMPTY
+    assert fwd(A, None, N, K, M, 0, h, 0, None, A, wsb) == CACHE_EMPTY
     # shape / recipe mismatch
-    r = L.fp8_linear_fwd(A, A, N, K, 512, 0, h, 1, A, ctypes.byref(sx), None, A,
-                         L.fp8_linear_workspace_bytes(N, K, 512, 0), None)
-    assert r == CACHE_MISMATCH
-    r = L.fp8_linear_fwd(A, A, N, K, M, 1, h, 1, A, ctypes.byref(sx), None, A,
-                         L.fp8_linear_workspace_bytes(N, K, M, 1), None)
-    assert r == CACHE_MISMATCH
+    assert fwd(A, A, N, K, 512, 0, h, 1, None, A, L.fp8_linear_workspace_bytes(N, K, 512, 0)) == CACHE_MISMATCH
+    assert fwd(A, A, N, K, M, 1, h, 1, None, A, L.fp8_linear_workspace_bytes(N, K, M, 1)) == CACHE_MISMATCH
     # bad flag, small workspace, None without w_q
-    assert L.fp8_linear_fwd(A, A, N, K, M, 0, h, 2, A, ctypes.byref(sx), None, A, wsb, None) == ENUM
-    assert L.fp8_linear_fwd(A, A, N, K, M, 0, h, 1, A, ctypes.byref(sx), None, A, 16, None) == WORKSPACE
-    assert L.fp8_linear_fwd(A, A, N, K, M, 0, None, -1, A, ctypes.byref(sx), None, A, wsb, None) == NULL
+    assert fwd(A, A, N, K, M, 0, h, 2, None, A, wsb) == ENUM
+    assert fwd(A, A, N, K, M, 0, h, 1, None, A, 16) == WORKSPACE
+    assert fwd(A, A, N, K, M, 0, None, -1, None, A, wsb) == NULL
     # every linear dimension is some GEMM's contraction: below 2^23
     big = 1 << 23
-    assert L.fp8_linear_fwd(A, A, big, K, M, 0, None, -1, A, ctypes.byref(sx), ctypes.byref(qt()), A,
-                            1 << 40, None) == SHAPE
-    assert L.fp8_linear_bwd(A, N, K, big, 0, ctypes.byref(sx), None, ctypes.byref(qt()), ctypes.byref(qt()), A, A,
-                            A, 1 << 40, None) == SHAPE
+    assert fwd(A, A, big, K, M, 0, None, -1, ctypes.byref(qt()), A, 1 << 40) == SHAPE
+    assert bwd(N, K, big, 0, None, ctypes.byref(qt()), ctypes.byref(qt()), A, A, A, 1 << 40) == SHAPE
+    # amax hand-off: tensorwise recipe only, 16-byte aligned, dX partials need dX
+    wsb1 = L.fp8_linear_workspace_bytes(N, K, M, 1)
+    assert fwd(A, A, N, K, M, 1, None, -1, ctypes.byref(qt()), A, wsb1, xa=A) == ENUM
+    assert fwd(A, A, N, K, M, 0, None, -1, ctypes.byref(qt()), A, wsb, ya=U) == ALIGN
+    assert bwd(N, K, M, 1, None, ctypes.byref(qt()), ctypes.byref(qt()), A, A, A, wsb1, dya=A) == ENUM
+    assert bwd(N, K, M, 0, None, ctypes.byref(qt()), ctypes.byref(qt()), None, A, A, wsb, dxa=A) == NULL
     # backward through an empty cache
     dq = qt()
-    r = L.fp8_linear_bwd(A, N, K, M, 0, ctypes.byref(sx), h, None, ctypes.byref(dq), A, A, A, wsb, None)
-    assert r == CACHE_EMPTY
-    assert L.fp8_linear_bwd(A, N, K, M, 0, ctypes.byref(sx), h, None, ctypes.byref(dq), None, None, A,
-                            wsb, None) == NULL
+    assert bwd(N, K, M, 0, h, None, ctypes.byref(dq), A, A, A, wsb) == CACHE_EMPTY
+    assert bwd(N, K, M, 0, h, None, ctypes.byref(dq), None, None, A, wsb) == NULL
     assert L.fp8_wcache_valid(h) == 0          # nothing above filled it
     L.fp8_wcache_destroy(h)
     L.fp8_wcache_destroy(None)
