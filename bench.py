@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-stage breakdown")
-    ap.add_argument("--no-block", action="store_true", help="skip the block-scaling run")
+    ap.add_argument("--no-block", action="store_true", help="skip the block-scaling run and the stacked-linear amax hand-off run")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after the steps, negate a 512 MiB fp16 tensor (counter calibration)")
     ap.add_argument("--summarize", metavar="PREFIX", help="summarize PREFIX_kernel_trace.csv / "
@@ -343,6 +343,49 @@ def time_steps(torch, layers, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def chain_times(fp8, torch, synth, N, steps, warmup, dev):
+    """The two linears stacked (512 -> 2048 -> 512: Y1 is X2, dX2 is dY1),
+    tensorwise, timed without and with the amax hand-off: with it the
+    forward GEMM of layer 1 emits Y1's amax partials and layer 2 quantizes X2
+    in one pass; the data-gradient GEMM of layer 2 does the same for dY1."""
+    (K1, M1), (K2, M2) = SHAPES
+    x1, w1, _ = synth.operands_on_device(N, K1, M1, seed=0, device=dev)
+    _, w2, dy2 = synth.operands_on_device(N, K2, M2, seed=1, device=dev)
+    l1 = fp8.Fp8Linear(N, K1, M1, device=dev)
+    l2 = fp8.Fp8Linear(N, K2, M2, device=dev)
+    y1 = torch.empty((N, M1), dtype=torch.bfloat16, device=dev)
+    y2 = torch.empty((N, M2), dtype=torch.bfloat16, device=dev)
+    dx2 = torch.empty((N, K2), dtype=torch.bfloat16, device=dev)
+    dx1 = torch.empty((N, K1), dtype=torch.bfloat16, device=dev)
+    dw1 = torch.empty((M1, K1), dtype=torch.bfloat16, device=dev)
+    dw2 = torch.empty((M2, K2), dtype=torch.bfloat16, device=dev)
+    pa, pb = fp8.amax_partials(dev), fp8.amax_partials(dev)
+
+    def step(h):
+        l1.forward(x1, w1, y=y1, y_amax=pa if h else None)
+        l2.forward(y1, w2, y=y2, x_amax=pa if h else None)
+        l2.backward(dy2, dx=dx2, dw=dw2, dx_amax=pb if h else None)
+        l1.backward(dx2, dx=dx1, dw=dw1, dy_amax=pb if h else None)
+
+    res = {}
+    for h in (False, True):
+        for _ in range(warmup):
+            step(h)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step(h)
+        e1.record()
+        torch.cuda.synchronize()
+        res[h] = e0.elapsed_time(e1) / steps
+    flops = sum(6 * N * K * M for K, M in SHAPES)
+    return {"workload": "512->2048->512 stack (Y1 = X2, dX2 = dY1), N=%d, tensorwise" % N,
+            "ms_per_step": round(res[False], 4), "ms_per_step_handoff": round(res[True], 4),
+            "value": round(flops / (res[False] / 1e3) / 1e12, 2),
+            "value_handoff": round(flops / (res[True] / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
+
+
 def measured_traffic(stage):
     """HBM bytes per launch of `stage` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or None when
@@ -460,6 +503,13 @@ def main():
                  "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in st.items()} for st in bst],
                  "roofline": roofline_of(max(bst, key=lambda st: st["ms"]))}
         block["roofline"]["traffic"] = None
+        del blayers
+        torch.cuda.empty_cache()
+    chain = None
+    if not args.no_block:
+        chain = chain_times(fp8, torch, synth, N, args.steps, args.warmup, dev)
+        print("stacked linears: %.4f ms/step, with the amax hand-off %.4f ms/step" %
+              (chain["ms_per_step"], chain["ms_per_step_handoff"]), file=sys.stderr, flush=True)
     pages_tflops = sum(6 * 131072 * K * M for K, M in shapes) / (sum(PAGES_MS[s] for s in shapes) / 1e3) / 1e12
 
     out = {
@@ -477,6 +527,7 @@ def main():
         "roofline": roofline_of(dom),
         "cpu_baseline": None,
         "block_scaling": block,
+        "amax_handoff": chain,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens)
