@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-stage breakdown")
-    ap.add_argument("--no-block", action="store_true", help="skip the block-scaling run and the stacked-linear amax hand-off run")
+    ap.add_argument("--no-block", action="store_true", help="skip the block-scaling, stacked-linear (amax hand-off) and BF16 comparator runs")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after the steps, negate a 512 MiB fp16 tensor (counter calibration)")
     ap.add_argument("--summarize", metavar="PREFIX", help="summarize PREFIX_kernel_trace.csv / "
@@ -386,6 +386,35 @@ def chain_times(fp8, torch, synth, N, steps, warmup, dev):
             "value_handoff": round(flops / (res[True] / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
 
 
+def bf16_comparator(torch, synth, N, steps, warmup, dev):
+    """The pages' baseline: the same two linears' forward + backward in BF16
+    (no quantization), each product one hipBLASLt GEMM through torch.mm with
+    bf16 output; right-hand operands contiguous."""
+    ops = []
+    for idx, (K, M) in enumerate(SHAPES):
+        x, w, dy = synth.operands_on_device(N, K, M, seed=idx, device=dev)
+        ops.append((x, w, w.t().contiguous(), dy))
+
+    def step():
+        for x, w, wt, dy in ops:
+            torch.mm(x, wt)            # Y = X W^T
+            torch.mm(dy, w)            # dX = dY W
+            torch.mm(dy.t(), x)        # dW = dY^T X
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = sum(6 * N * K * M for K, M in SHAPES)
+    return {"workload": "the same two linears in BF16 (hipBLASLt via torch.mm, bf16 out), N=%d" % N,
+            "ms_per_step": round(ms, 4), "value": round(flops / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
+
+
 def measured_traffic(stage):
     """HBM bytes per launch of `stage` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or None when
@@ -510,6 +539,12 @@ def main():
         chain = chain_times(fp8, torch, synth, N, args.steps, args.warmup, dev)
         print("stacked linears: %.4f ms/step, with the amax hand-off %.4f ms/step" %
               (chain["ms_per_step"], chain["ms_per_step_handoff"]), file=sys.stderr, flush=True)
+    bf16 = None
+    if not args.no_block:
+        bf16 = bf16_comparator(torch, synth, N, args.steps, args.warmup, dev)
+        bf16["fp8_speedup"] = round(bf16["ms_per_step"] / ms, 3)
+        print("bf16 comparator: %.4f ms/step (FP8 step %.2fx faster)" % (bf16["ms_per_step"], bf16["fp8_speedup"]),
+              file=sys.stderr, flush=True)
     pages_tflops = sum(6 * 131072 * K * M for K, M in shapes) / (sum(PAGES_MS[s] for s in shapes) / 1e3) / 1e12
 
     out = {
@@ -528,6 +563,7 @@ def main():
         "cpu_baseline": None,
         "block_scaling": block,
         "amax_handoff": chain,
+        "bf16_comparator": bf16,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens)
