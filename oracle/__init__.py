@@ -62,6 +62,7 @@ def _load():
         "orc_amax_bf16": (F, [P, I64]),
         "orc_scale_from_amax": (None, [F, I, P, P]),
         "orc_quant_tensor": (None, [P, I64, I64, I, P, P, P, P, P]),
+        "orc_quant_delayed": (None, [P, I64, I64, I, P, I64, P, P, P, P, P]),
         "orc_quant_block_1x128": (None, [P, I64, I64, I, P, P, P, P, P, P]),
         "orc_quant_block_128x128": (None, [P, I64, I64, I, P, P, P, P]),
         "orc_gemm_tensor": (None, [P, I, P, I, I64, I64, I64, F, F, P, P, P]),
@@ -159,6 +160,24 @@ def quant_tensor(x, fmt, row=True, col=True):
     _load().orc_quant_tensor(_p(x), R, C, FORMATS[fmt], _p(q_row), _p(q_col),
                              _p(amax), _p(s), _p(si))
     return {"q_row": q_row, "q_col": q_col, "amax": amax[0], "scale": s[0], "scale_inv": si[0]}
+
+
+def quant_delayed(x, fmt, history, row=True, col=True):
+    """Delayed tensorwise scaling: scale from max(history) (previous calls'
+    amaxes, most recent first), then this call's amax is pushed in front.
+    x: uint16 [R, C]; history: float32 [H].  Returns the codes, scales, this
+    call's amax and the new history (the argument is not modified)."""
+    x = _c(x, np.uint16)
+    R, C = x.shape
+    h = np.array(history, dtype=np.float32, copy=True)
+    q_row = np.empty((R, C), np.uint8) if row else None
+    q_col = np.empty((C, R), np.uint8) if col else None
+    amax = np.zeros(1, np.float32)
+    s = np.zeros(1, np.float32)
+    si = np.zeros(1, np.float32)
+    _load().orc_quant_delayed(_p(x), R, C, FORMATS[fmt], _p(h), h.size, _p(q_row), _p(q_col),
+                              _p(amax), _p(s), _p(si))
+    return {"q_row": q_row, "q_col": q_col, "amax": amax[0], "scale": s[0], "scale_inv": si[0], "history": h}
 
 
 def quant_block_1x128(x, fmt, row=True, col=True):

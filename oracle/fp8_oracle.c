@@ -229,6 +229,38 @@ void orc_quant_tensor(const uint16_t* x, int64_t R, int64_t C, int f,
         }
 }
 
+/* Delayed tensorwise scaling with an amax history (the DelayedScaling case
+ * the weight-caching issue contrasts with block scaling: TransformerEngine
+ * issue 2852, opening post and question 3).  Readings (not on the pages):
+ * hist[0..H-1] holds the amaxes of the tensor's previous quantize calls, most
+ * recent first; the scale comes from the largest of them (NaN if any is NaN),
+ * by the same rules as current scaling; then this call's amax is pushed in
+ * front and the oldest entry dropped.  A history of zeros gives scale 1. */
+void orc_quant_delayed(const uint16_t* x, int64_t R, int64_t C, int f, float* hist, int64_t H,
+                       uint8_t* q_row, uint8_t* q_col,
+                       float* amax_out, float* scale_out, float* sinv_out) {
+    float hmax = 0.0f;
+    for (int64_t i = 0; i < H; i++) {
+        if (isnan(hist[i])) { hmax = NAN; break; }
+        if (hist[i] > hmax) hmax = hist[i];
+    }
+    float s, si;
+    orc_scale_from_amax(hmax, f, &s, &si);
+    *scale_out = s;
+    *sinv_out = si;
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++)
+        for (int64_t c = 0; c < C; c++) {
+            uint8_t q = quant_elem(x[r * C + c], s, f);
+            if (q_row) q_row[r * C + c] = q;
+            if (q_col) q_col[c * R + r] = q;
+        }
+    float amax = orc_amax_bf16(x, R * C);
+    if (amax_out) *amax_out = amax;
+    for (int64_t i = H - 1; i > 0; i--) hist[i] = hist[i - 1];
+    hist[0] = amax;
+}
+
 /* 1x128 blocks.  Row layout: one block per (row r, 128 columns), scales
  * s_row[R][C/128].  Col layout: one block per (column c, 128 rows), scales
  * s_col[C][R/128]; q_col[c][r] uses the scale of block (c, r/128). */
