@@ -19,7 +19,7 @@ from ._lib import (E4M3, E5M2, LAYOUT_COL, LAYOUT_ROW, RECIPE_BLOCK, RECIPE_TENS
 __all__ = ["block_gemm_scale", "E4M3", "E5M2", "SCALE_TENSOR", "SCALE_1x128", "SCALE_128x128", "RECIPE_TENSOR",
            "RECIPE_BLOCK", "LAYOUT_ROW", "LAYOUT_COL", "Fp8Error", "QTensor", "quantize",
            "gemm", "WeightCache", "Fp8Linear", "linear_workspace", "lib", "amax_partials",
-           "AMAX_PARTIALS_BYTES"]
+           "AMAX_PARTIALS_BYTES", "quantize_delayed"]
 
 
 def lib():
@@ -110,6 +110,27 @@ def quantize(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=
     oc = out.c()
     _lib.check(L.fp8_quantize(_ptr(x), R, C, fmt, scaling, layouts, ctypes.byref(oc), _ptr(ws), wsb,
                               _stream(stream)))
+    return out
+
+
+def quantize_delayed(x, fmt, history, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None):
+    """Delayed tensorwise scaling: encode with FMAX / max(history), then roll
+    the fp32 device tensor `history` (most recent amax first) and store
+    amax(x) in front.  Returns the QTensor (out.amax = amax(x))."""
+    L = lib()
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    if history.dtype != torch.float32 or history.dim() != 1 or not history.is_contiguous():
+        raise ValueError("history must be a contiguous 1-D float32 tensor")
+    x = x.contiguous()
+    R, C = x.shape
+    if out is None:
+        out = QTensor(R, C, SCALE_TENSOR, _dev(x), row=bool(layouts & LAYOUT_ROW), col=bool(layouts & LAYOUT_COL))
+    wsb = L.fp8_quantize_delayed_workspace_bytes(R, C)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
+    oc = out.c()
+    _lib.check(L.fp8_quantize_delayed(_ptr(x), R, C, fmt, layouts, ctypes.byref(oc), _ptr(history), history.numel(),
+                                      _ptr(ws), wsb, _stream(stream)))
     return out
 
 

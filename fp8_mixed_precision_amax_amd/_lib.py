@@ -22,7 +22,8 @@ STATUS = {0: "FP8_OK", 1: "FP8_ERR_NULL", 2: "FP8_ERR_SHAPE", 3: "FP8_ERR_ALIGN"
 
 # every symbol include/fp8_linear.h declares
 EXPORTS = [
-    "fp8_quantize_workspace_bytes", "fp8_quantize", "fp8_quantize_from_amax", "fp8_gemm_workspace_bytes",
+    "fp8_quantize_workspace_bytes", "fp8_quantize", "fp8_quantize_from_amax",
+    "fp8_quantize_delayed_workspace_bytes", "fp8_quantize_delayed", "fp8_gemm_workspace_bytes",
     "fp8_gemm", "fp8_gemm_amax",
     "fp8_wcache_create", "fp8_wcache_invalidate", "fp8_wcache_valid", "fp8_wcache_fills",
     "fp8_wcache_destroy", "fp8_linear_workspace_bytes", "fp8_linear_fwd", "fp8_linear_bwd",
@@ -75,6 +76,8 @@ def load():
         "fp8_linear_fwd": (I, [P, P, I64, I64, I64, I, P, I, P, QP, QP, P, P, P, SZ, P]),
         "fp8_linear_bwd": (I, [P, I64, I64, I64, I, QP, P, QP, QP, P, P, P, P, P, SZ, P]),
         "fp8_quantize_from_amax": (I, [P, I64, I64, I, U, QP, P, P]),
+        "fp8_quantize_delayed_workspace_bytes": (SZ, [I64, I64]),
+        "fp8_quantize_delayed": (I, [P, I64, I64, I, U, QP, P, I64, P, SZ, P]),
         "fp8_gemm_amax": (I, [P, I, GemmScaleC, P, I, GemmScaleC, I64, I64, I64, P, P, P, SZ, P]),
         "fp8_status_string": (ctypes.c_char_p, [I]),
         "fp8_last_error": (ctypes.c_char_p, []),

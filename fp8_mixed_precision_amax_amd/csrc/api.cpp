@@ -126,6 +126,8 @@ fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, in
     q.amax = scaling == FP8_SCALE_TENSOR ? out->amax : nullptr;
     q.partial = given_amax ? static_cast<uint16_t*>(const_cast<void*>(given_amax)) : static_cast<uint16_t*>(ws);
     q.partial_given = given_amax != nullptr;
+    q.hist = nullptr;
+    q.hist_len = 0;
     return hip_status(fp8k::launch_quantize(q, st), "quantize launch");
 }
 
@@ -224,6 +226,43 @@ fp8_status fp8_quantize_from_amax(const void* x, int64_t rows, int64_t cols, fp8
     FP8_TRY(check_ptr16("amax_partials", amax_partials));
     return do_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out, nullptr, static_cast<hipStream_t>(stream),
                        amax_partials);
+}
+
+size_t fp8_quantize_delayed_workspace_bytes(int64_t rows, int64_t cols) {
+    // one 16-bit amax per 128x128 tile, rounded up to 16 bytes
+    if (!dim_ok(rows) || !dim_ok(cols)) return 0;
+    const size_t tiles = (size_t)(rows / 128) * (size_t)(cols / 128);
+    return (tiles * 2 + 15) & ~(size_t)15;
+}
+
+fp8_status fp8_quantize_delayed(const void* x, int64_t rows, int64_t cols, fp8_format format, unsigned layouts,
+                                const fp8_qtensor* out, float* amax_history, int64_t history_len, void* ws,
+                                size_t ws_bytes, void* stream) {
+    FP8_TRY(check_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out));
+    if (history_len < 1 || history_len > fp8k::kMaxHistory)
+        return fail(FP8_ERR_SHAPE, "history_len %lld: must be 1 .. %d", (long long)history_len, fp8k::kMaxHistory);
+    FP8_TRY(check_ptr4("amax_history", amax_history));
+    const size_t need = fp8_quantize_delayed_workspace_bytes(rows, cols);
+    if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    FP8_TRY(check_ptr16("ws", ws));
+    fp8k::QuantizeLaunch q;
+    q.x = x;
+    q.rows = rows;
+    q.cols = cols;
+    q.format = format;
+    q.scaling = 3;
+    q.q_row = (layouts & FP8_LAYOUT_ROW) ? out->q_row : nullptr;
+    q.q_col = (layouts & FP8_LAYOUT_COL) ? out->q_col : nullptr;
+    q.scale = out->scale;
+    q.scale_inv = out->scale_inv;
+    q.scale_col = nullptr;
+    q.scale_inv_col = nullptr;
+    q.amax = out->amax;
+    q.partial = static_cast<uint16_t*>(ws);
+    q.partial_given = false;
+    q.hist = amax_history;
+    q.hist_len = (int)history_len;
+    return hip_status(fp8k::launch_quantize(q, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
 size_t fp8_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K) { return fp8k::gemm_ws_bytes(I, J, K); }

@@ -62,6 +62,20 @@ __device__ __forceinline__ void scale_from_amax_bits(uint32_t m, float& s, float
     si = 1.0f / s;
 }
 
+// Scale from an fp32 amax >= 0 or NaN (the largest entry of an amax
+// history): scale = FMAX / amax (IEEE fp32 division), 1 for amax 0 / +Inf /
+// NaN, FLT_MAX if the division overflows; scale_inv = 1 / scale.
+template <int FMT>
+__device__ __forceinline__ void scale_from_amax_f32(float amax, float& s, float& si) {
+    if (!(amax > 0.0f) || __builtin_isinf(amax)) {
+        s = 1.0f;
+    } else {
+        s = FmtTraits<FMT>::fmax / amax;
+        if (__builtin_isinf(s)) s = 3.40282346638528859812e+38f;
+    }
+    si = 1.0f / s;
+}
+
 // Four fp32 values -> four FP8 codes (byte 0 = a), round to nearest even,
 // saturating: values are clamped to [-FMAX, FMAX] before the hardware
 // conversion.  NaN inputs are patched separately (patch_nan8).

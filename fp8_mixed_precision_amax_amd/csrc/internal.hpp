@@ -8,12 +8,13 @@
 namespace fp8k {
 
 constexpr int kMaxAmaxPartials = 2048;   // 16-bit slots, a multiple of 512
+constexpr int kMaxHistory = 1024;        // longest amax history of delayed scaling
 
 struct QuantizeLaunch {
     const void* x;      // [rows, cols] bf16
     int64_t rows, cols;
     int format;         // 0 E4M3, 1 E5M2
-    int scaling;        // 0 tensor, 1 1x128, 2 128x128
+    int scaling;        // 0 tensor, 1 1x128, 2 128x128, 3 tensor with delayed scaling
     void* q_row;        // may be null
     void* q_col;        // may be null
     float* scale;
@@ -24,6 +25,8 @@ struct QuantizeLaunch {
     uint16_t* partial;  // tensor: kMaxAmaxPartials 16-bit slots of scratch (16-byte aligned)
     bool partial_given; // tensor: partial already holds the amax partials of x (written by
                         // the producer of x); the amax pass is skipped
+    float* hist;        // delayed: amax history [hist_len], most recent first (read, then rolled);
+    int hist_len;       // partial then holds one 16-bit amax per 128x128 tile
 };
 
 int amax_partial_count(int64_t numel);

@@ -73,6 +73,9 @@ struct CastArgs {
     float* scale_inv_col;
     float* amax_out;    // tensor only, optional
     const uint16_t* partial;  // tensor only: kMaxAmaxPartials amax partials of pass 1 (unused slots 0)
+    const float* hist;        // delayed only: amax history [hist_len]
+    int hist_len;
+    uint16_t* tile_amax;      // delayed only: amax of each 128x128 tile (bf16 magnitude bits)
 };
 
 template <int FMT, int MODE>
@@ -101,6 +104,15 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
         for (int r = 0; r < kMaxAmaxPartials / 512; r++)
             pw[r] = reinterpret_cast<const uint4*>(a.partial)[r * 64 + lane];
     }
+    // delayed: the amax history, likewise first
+    float hv[kMaxHistory / 64];
+    if constexpr (MODE == 3) {
+#pragma unroll
+        for (int r = 0; r < kMaxHistory / 64; r++) {
+            const int idx = r * 64 + lane;
+            hv[r] = idx < a.hist_len ? a.hist[idx] : 0.0f;
+        }
+    }
 
     // ---- load 32 rows x 8 bf16 ------------------------------------------
     uint4 v[32];
@@ -108,7 +120,7 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     for (int i = 0; i < 32; i++) v[i] = ld_nt16(a.x + FP8K_ROW(i) * a.C + col0);
 
     // ---- scales ---------------------------------------------------------
-    float s_tile = 1.0f;          // MODE 0 and 2
+    float s_tile = 1.0f;          // MODE 0, 2 and 3
     bool nan_any = false;
     if constexpr (MODE == 0) {
         uint32_t m = 0;
@@ -123,6 +135,31 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
             a.scale[0] = s_tile;
             a.scale_inv[0] = si;
             if (a.amax_out) a.amax_out[0] = m > 0x7F80u ? __uint_as_float(0x7FC00000u) : __uint_as_float(m << 16);
+        }
+    } else if constexpr (MODE == 3) {
+        // scale from the largest history entry (NaN if any entry is NaN)
+        float hm = 0.0f;
+        bool hn = false;
+#pragma unroll
+        for (int r = 0; r < kMaxHistory / 64; r++) {
+            hn |= hv[r] != hv[r];
+            hm = hv[r] > hm ? hv[r] : hm;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) hm = fmaxf(hm, __shfl_xor(hm, o, 64));
+        float si;
+        scale_from_amax_f32<FMT>(__ballot(hn) != 0 ? __uint_as_float(0x7FC00000u) : hm, s_tile, si);
+        // this tile's amax, for the history update and the NaN patch
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < 32; i++)
+            m = pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v[i].x), mag2(v[i].y)), pkmax_u16(mag2(v[i].z), mag2(v[i].w))));
+        m = wave_max_u32(hmax_u16(m));
+        nan_any = m > 0x7F80u;
+        if (lane == 0) a.tile_amax[tile] = (uint16_t)m;
+        if (slot == 0 && lane == 0) {
+            a.scale[0] = s_tile;
+            a.scale_inv[0] = si;
         }
     } else if constexpr (MODE == 2) {
         uint32_t m = 0;
@@ -139,7 +176,7 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
         }
     }
 
-    if constexpr (MODE == 0 || MODE == 2) {
+    if constexpr (MODE == 0 || MODE == 2 || MODE == 3) {
         // One scale for the whole tile: the column layout is the transpose
         // of the row layout.
         uint2 code[32];
@@ -278,6 +315,37 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
 #undef FP8K_ROW
 }
 
+// Delayed scaling, after the cast: this call's amax from the per-tile maxima,
+// then the history rolls by one (oldest entry dropped) and takes it in front.
+__global__ __launch_bounds__(256) void history_update_kernel(const uint16_t* __restrict__ tile_amax, int64_t ntiles,
+                                                             float* __restrict__ hist, int H, float* amax_out) {
+    uint32_t m = 0;
+    for (int64_t i = threadIdx.x; i < ntiles; i += 256) m = m > tile_amax[i] ? m : tile_amax[i];
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = red[0];
+    for (int w = 1; w < 4; w++) m = m > red[w] ? m : red[w];
+    const float amax = m > 0x7F80u ? __uint_as_float(0x7FC00000u) : __uint_as_float(m << 16);
+    float v[kMaxHistory / 256];
+#pragma unroll
+    for (int k = 0; k < kMaxHistory / 256; k++) {
+        const int i = (int)threadIdx.x + 256 * k;
+        v[k] = i + 1 < H ? hist[i] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxHistory / 256; k++) {
+        const int i = (int)threadIdx.x + 256 * k;
+        if (i + 1 < H) hist[i + 1] = v[k];
+    }
+    if (threadIdx.x == 0) {
+        hist[0] = amax;
+        if (amax_out) amax_out[0] = amax;
+    }
+}
+
 int amax_partial_count(int64_t numel) {
     // about eight workgroups per CU, one 16-byte load per thread per sweep step
     const int64_t n16 = numel / 8;
@@ -300,6 +368,9 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     a.scale_inv_col = q.scale_inv_col;
     a.amax_out = q.amax;
     a.partial = q.partial;
+    a.hist = q.hist;
+    a.hist_len = q.hist_len;
+    a.tile_amax = q.partial;
     if (q.scaling == 0 && !q.partial_given) {
         const int g = amax_partial_count(q.rows * q.cols);
         hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(kAmaxThreads), 0, stream,
@@ -313,13 +384,21 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     if (q.format == 0) {
         if (q.scaling == 0) FP8K_CAST(0, 0);
         else if (q.scaling == 1) FP8K_CAST(0, 1);
-        else FP8K_CAST(0, 2);
+        else if (q.scaling == 2) FP8K_CAST(0, 2);
+        else FP8K_CAST(0, 3);
     } else {
         if (q.scaling == 0) FP8K_CAST(1, 0);
         else if (q.scaling == 1) FP8K_CAST(1, 1);
-        else FP8K_CAST(1, 2);
+        else if (q.scaling == 2) FP8K_CAST(1, 2);
+        else FP8K_CAST(1, 3);
     }
 #undef FP8K_CAST
+    if (q.scaling == 3) {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(history_update_kernel, dim3(1), dim3(256), 0, stream, q.partial, ntiles, q.hist,
+                           q.hist_len, q.amax);
+    }
     return hipGetLastError();
 }
 

@@ -175,6 +175,27 @@ fp8_status fp8_quantize_from_amax(const void* x_bf16, int64_t rows, int64_t cols
                                   void* stream);
 
 /*
+ * Delayed tensorwise scaling with an amax history: the DelayedScaling case
+ * the weight-caching issue contrasts with block scaling ("FP8 weight caching
+ * shows no speedup ... under Float8BlockScaling", TransformerEngine issue
+ * 2852: the opening post and its third question).  amax_history
+ * [history_len] (device fp32, 1 .. 1024 entries) holds the amaxes of this
+ * tensor's previous quantize calls, most recent first.  The call encodes x
+ * with scale = FMAX / max(history) (the current-scaling rules: 1 for a
+ * history max of 0, +Inf or NaN, FLT_MAX on overflow), writes out->scale,
+ * out->scale_inv (and out->amax, if non-NULL, with amax(x)), then rolls the
+ * history by one entry and stores amax(x) in front.  One pass over x (the
+ * encode needs no amax of x).  Workspace: one 16-bit amax per 128x128 tile,
+ * fp8_quantize_delayed_workspace_bytes.  Calls that share a history must be
+ * ordered (same stream); every call rolls it, so skipping a call (a cached
+ * weight) changes the scales of later calls.
+ */
+size_t fp8_quantize_delayed_workspace_bytes(int64_t rows, int64_t cols);
+fp8_status fp8_quantize_delayed(const void* x_bf16, int64_t rows, int64_t cols, fp8_format format,
+                                unsigned layouts, const fp8_qtensor* out, float* amax_history,
+                                int64_t history_len, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Scale of an FP8 GEMM operand (dequantisation factors):
  *   group == 0:  tensorwise, the factor is scale_inv[0]
  *   group >= 1:  the factor of operand row r in contraction block kb

@@ -79,6 +79,14 @@ def test_quantize_argument_errors(L):
     assert L.fp8_quantize_from_amax(A, 256, 256, 0, 3, ctypes.byref(qt()), None, None) == NULL
     assert L.fp8_quantize_from_amax(A, 256, 256, 0, 3, ctypes.byref(qt()), U, None) == ALIGN
     assert L.fp8_quantize_from_amax(A, 200, 256, 0, 3, ctypes.byref(qt()), A, None) == SHAPE
+    # delayed scaling: 1 .. 1024 history entries, a history, enough workspace
+    wsd = L.fp8_quantize_delayed_workspace_bytes(256, 256)
+    assert wsd == 16                          # 4 tiles x 2 bytes, rounded to 16
+    dq = lambda hist=A, H=16, ws=A, wsb=wsd: L.fp8_quantize_delayed(A, 256, 256, 0, 3, ctypes.byref(qt()), hist, H, ws,
+                                                                     wsb, None)
+    assert dq(H=0) == SHAPE and dq(H=1025) == SHAPE
+    assert dq(hist=None) == NULL
+    assert dq(wsb=8) == WORKSPACE
 
 
 def test_last_error_message(L):
