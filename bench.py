@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-stage breakdown")
-    ap.add_argument("--no-block", action="store_true", help="skip the block-scaling, stacked-linear (amax hand-off) and BF16 comparator runs")
+    ap.add_argument("--no-block", action="store_true", help="skip the block-scaling, stacked-linear (amax hand-off), BF16 comparator and delayed-scaling runs")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after the steps, negate a 512 MiB fp16 tensor (counter calibration)")
     ap.add_argument("--summarize", metavar="PREFIX", help="summarize PREFIX_kernel_trace.csv / "
@@ -415,6 +415,34 @@ def bf16_comparator(torch, synth, N, steps, warmup, dev):
             "ms_per_step": round(ms, 4), "value": round(flops / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
 
 
+def delayed_quant_times(fp8, torch, synth, N, reps, dev):
+    """Quantize of a dY-sized tensor (N x 2048, E5M2, both layouts): delayed
+    scaling (scale from a 1024-entry amax history, one pass: 2 B read + 2 B
+    written per element) against current scaling (amax pass + cast: 6 B)."""
+    M = SHAPES[0][1]
+    _, _, dy = synth.operands_on_device(N, SHAPES[0][0], M, seed=0, device=dev)
+    hist = torch.zeros(1024, dtype=torch.float32, device=dev)
+    qd = fp8.QTensor(N, M, fp8.SCALE_TENSOR, dev)
+    qc = fp8.QTensor(N, M, fp8.SCALE_TENSOR, dev)
+    res = {}
+    for name, fn in (("delayed", lambda: fp8.quantize_delayed(dy, fp8.E5M2, hist, out=qd)),
+                     ("current", lambda: fp8.quantize(dy, fp8.E5M2, out=qc))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+    n = N * M
+    return {"workload": "dY %dx%d E5M2, both layouts; delayed: 1024-entry amax history" % (N, M),
+            "ms_delayed": round(res["delayed"], 4), "gbs_delayed": round(4 * n / res["delayed"] / 1e6, 1),
+            "ms_current": round(res["current"], 4), "gbs_current": round(6 * n / res["current"] / 1e6, 1)}
+
+
 def measured_traffic(stage):
     """HBM bytes per launch of `stage` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or None when
@@ -545,6 +573,11 @@ def main():
         bf16["fp8_speedup"] = round(bf16["ms_per_step"] / ms, 3)
         print("bf16 comparator: %.4f ms/step (FP8 step %.2fx faster)" % (bf16["ms_per_step"], bf16["fp8_speedup"]),
               file=sys.stderr, flush=True)
+    delayed = None
+    if not args.no_block:
+        delayed = delayed_quant_times(fp8, torch, synth, N, args.reps, dev)
+        print("delayed-scaling quantize %.4f ms (%.0f GB/s), current scaling %.4f ms" %
+              (delayed["ms_delayed"], delayed["gbs_delayed"], delayed["ms_current"]), file=sys.stderr, flush=True)
     pages_tflops = sum(6 * 131072 * K * M for K, M in shapes) / (sum(PAGES_MS[s] for s in shapes) / 1e3) / 1e12
 
     out = {
@@ -564,6 +597,7 @@ def main():
         "block_scaling": block,
         "amax_handoff": chain,
         "bf16_comparator": bf16,
+        "delayed_scaling_quantize": delayed,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens)
