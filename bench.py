@@ -67,7 +67,7 @@ def parse():
 
 SHAPES = [(512, 2048), (2048, 512)]
 KINDS = (("amax_partial_kernel", "amax"), ("cast_kernel", "cast"), ("gemm_block_kernel", "gemm"),
-         ("gemm_tensor_kernel", "gemm"), ("splitk_reduce_kernel", "reduce"))
+         ("gemm_block_wide_kernel", "gemm"), ("gemm_tensor_kernel", "gemm"), ("splitk_reduce_kernel", "reduce"))
 COPY_BYTES = 2 * 512 * 1024 * 1024      # the --copy-reference kernel reads 512 MiB and writes 512 MiB
 
 
@@ -95,7 +95,8 @@ def kernel_kind(name):
 
 
 def short_name(name):
-    return name.replace("void ", "").replace("fp8k::", "").replace("tensor::", "").replace("block::", "")
+    return (name.replace("void ", "").replace("fp8k::", "").replace("tensor::", "").replace("blockw::", "")
+            .replace("block::", ""))
 
 
 def source_digest():
