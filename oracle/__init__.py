@@ -71,6 +71,12 @@ def _load():
         "orc_gemm_tensor_sampled": (None, [P, I, P, I, I64, F, F, P, P, I64, P, P]),
         "orc_gemm_block_sampled": (None, [P, I, P, I64, I64, I64, P, I, P, I64, I64, I64,
                                           I64, P, P, I64, P, P]),
+        "orc_gelu_f32": (F, [ctypes.c_uint16]),
+        "orc_gelu_grad_f32": (F, [ctypes.c_uint16]),
+        "orc_gelu_array": (None, [P, I64, P]),
+        "orc_gelu_f32_array": (None, [P, I64, P]),
+        "orc_gelu_grad_f32_array": (None, [P, I64, P]),
+        "orc_dgelu_array": (None, [P, P, I64, P]),
         "orc_num_threads": (I, []),
         "orc_set_num_threads": (None, [I]),
     }
@@ -379,3 +385,63 @@ def linear_bwd(dy, ctx):
     a, sa, b, sb = _gemm_operands_wgrad(dyq, ctx["xq"], scaling, N, K, M)
     dw = _gemm(a, "e5m2", sa, b, "e4m3", sb, scaling)
     return dx, dw, dyq
+
+
+# --------------------------------------------------------------------------
+# GELU between the two linears of an MLP block (exact erf form, fp64
+# evaluation rounded once to fp32; see fp8_oracle.c)
+# --------------------------------------------------------------------------
+
+def gelu_f32(x):
+    """fl32(GELU(x)) of bf16 bit patterns."""
+    x = _c(x, np.uint16)
+    out = np.empty(x.shape, np.float32)
+    _load().orc_gelu_f32_array(_p(x), x.size, _p(out))
+    return out
+
+
+def gelu_grad_f32(x):
+    """fl32(GELU'(x)) of bf16 bit patterns."""
+    x = _c(x, np.uint16)
+    out = np.empty(x.shape, np.float32)
+    _load().orc_gelu_grad_f32_array(_p(x), x.size, _p(out))
+    return out
+
+
+def gelu(x):
+    """The activation passed to the next linear: bf16(fl32(GELU(x)))."""
+    x = _c(x, np.uint16)
+    out = np.empty(x.shape, np.uint16)
+    _load().orc_gelu_array(_p(x), x.size, _p(out))
+    return out
+
+
+def dgelu(dy, x):
+    """The gradient passed back through GELU: bf16(fl32(dy * fl32(GELU'(x))))."""
+    dy, x = _c(dy, np.uint16), _c(x, np.uint16)
+    assert dy.shape == x.shape
+    out = np.empty(x.shape, np.uint16)
+    _load().orc_dgelu_array(_p(dy), _p(x), x.size, _p(out))
+    return out
+
+
+def quant_gelu(a, fmt, scaling, row=True, col=True):
+    """Quantize GELU(a) as the next linear's input: the activation first,
+    then the current-scaling quantizer on its bf16 values."""
+    return quantize(gelu(a), fmt, scaling, row, col)
+
+
+def quant_dgelu(dh, a, fmt, scaling, row=True, col=True):
+    """Quantize dGELU(dh, a) as the previous linear's incoming gradient."""
+    return quantize(dgelu(dh, a), fmt, scaling, row, col)
+
+
+def linear_fwd_gelu(a, w, scaling="tensor", wq=None):
+    """The second linear of an MLP block: Y = GELU(A) W^T."""
+    return linear_fwd(gelu(a), w, scaling, wq)
+
+
+def linear_bwd_dgelu(dh, a, ctx):
+    """The first linear of an MLP block, backward: its incoming gradient is
+    dGELU(dH, A), dH the gradient of GELU's output, A its pre-activation."""
+    return linear_bwd(dgelu(dh, a), ctx)

@@ -32,11 +32,16 @@
  *  - GEMMs accumulate in fp32 with k ascending; tensorwise epilogue is
  *    bf16(fl32(acc * fl32(sinvA * sinvB))); block mode promotes every
  *    128-long contraction block: acc = fl32(acc + fl32(p * fl32(sa * sb))).
+ *  - the GELU between an MLP block's two linears is the exact (erf) form,
+ *    GELU and GELU' each rounded once to fp32 from an fp64 evaluation; the
+ *    activation is bf16(fl32(GELU(x))), the gradient through it
+ *    bf16(fl32(dy * fl32(GELU'(x)))); NaN results are the quiet NaN 0x7FC0.
  *
  * Compile with -O2 -ffp-contract=off (no fused multiply-add, no fast-math).
  * Parity status: every function below is pinned by the CPU test-suite
  * (exhaustive code tables, brute-force encoders, exact integer GEMMs,
- * closed-form invariants); none is "parity unpinned".
+ * closed-form invariants, 45-digit evaluations of GELU and GELU' at every
+ * bf16 input); none is "parity unpinned".
  */
 #include <float.h>
 #include <math.h>
@@ -323,6 +328,62 @@ void orc_quant_block_128x128(const uint16_t* x, int64_t R, int64_t C, int f,
                     if (q_col) q_col[c * R + r] = q;
                 }
         }
+}
+
+/* ------------------------------------------------------------------ */
+/* GELU between the two linears of an MLP block.  The pages name no     */
+/* formula; the exact (erf) GELU is read:                               */
+/*   GELU(x)  = x Phi(x),  Phi(x) = erfc(-x / sqrt 2) / 2               */
+/*   GELU'(x) = Phi(x) + x phi(x),  phi(x) = exp(-x^2 / 2) / sqrt(2 pi) */
+/* each evaluated in fp64 and rounded once to fp32.  The activation     */
+/* passed on is bf16(fl32(GELU(x))); the gradient passed back is        */
+/* bf16(fl32(dy * fl32(GELU'(x)))), one fp32 multiply.  Every NaN result */
+/* is the canonical quiet NaN 0x7FC0 (GELU(-Inf) = -Inf * 0 is one).    */
+/* ------------------------------------------------------------------ */
+
+static const double ORC_SQRT1_2 = 0.70710678118654752440;       /* 1 / sqrt(2) */
+static const double ORC_INV_SQRT_2PI = 0.39894228040143267794;  /* 1 / sqrt(2 pi) */
+
+float orc_gelu_f32(uint16_t x) {
+    double a = (double)orc_dec_bf16(x);
+    double phi_cdf = 0.5 * erfc(-a * ORC_SQRT1_2);
+    return (float)(a * phi_cdf);
+}
+
+float orc_gelu_grad_f32(uint16_t x) {
+    double a = (double)orc_dec_bf16(x);
+    double phi_cdf = 0.5 * erfc(-a * ORC_SQRT1_2);
+    double phi_pdf = exp(-0.5 * a * a) * ORC_INV_SQRT_2PI;
+    double g = phi_cdf + a * phi_pdf;
+    /* below x = -38 both terms underflow in fp64 and their sum is +0; the
+     * exact value is negative there (x phi(x) dominates), so it rounds to -0 */
+    if (g == 0.0 && a < 0.0) g = -0.0;
+    return (float)g;
+}
+
+static uint16_t bf16_canon(float v) { return isnan(v) ? (uint16_t)0x7FC0 : orc_bf16_rne(v); }
+
+void orc_gelu_array(const uint16_t* x, int64_t n, uint16_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) out[i] = bf16_canon(orc_gelu_f32(x[i]));
+}
+
+void orc_gelu_f32_array(const uint16_t* x, int64_t n, float* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) out[i] = orc_gelu_f32(x[i]);
+}
+
+void orc_gelu_grad_f32_array(const uint16_t* x, int64_t n, float* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) out[i] = orc_gelu_grad_f32(x[i]);
+}
+
+void orc_dgelu_array(const uint16_t* dy, const uint16_t* x, int64_t n, uint16_t* out) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; i++) {
+        float p = orc_dec_bf16(dy[i]) * orc_gelu_grad_f32(x[i]);   /* one fp32 rounding */
+        out[i] = bf16_canon(p);
+    }
 }
 
 /* ------------------------------------------------------------------ */
