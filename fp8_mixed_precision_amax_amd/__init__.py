@@ -134,6 +134,60 @@ def quantize_delayed(x, fmt, history, layouts=LAYOUT_ROW | LAYOUT_COL, out=None,
     return out
 
 
+def _bf16_pair(name, *ts):
+    for t in ts:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(name + ": tensors must be contiguous bfloat16")
+    if any(t.shape != ts[0].shape for t in ts):
+        raise ValueError(name + ": shapes differ")
+
+
+def gelu(x, out=None, stream=None):
+    """GELU(x) elementwise (exact erf form), bf16 in and out (fp8_gelu)."""
+    _bf16_pair("gelu", x)
+    if out is None:
+        out = torch.empty_like(x)
+    _lib.check(lib().fp8_gelu(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out
+
+
+def dgelu(dy, x, out=None, stream=None):
+    """dy * GELU'(x) elementwise, bf16 in and out (fp8_dgelu): dy is the
+    gradient of GELU's output, x GELU's input."""
+    _bf16_pair("dgelu", dy, x)
+    if out is None:
+        out = torch.empty_like(x)
+    _lib.check(lib().fp8_dgelu(_ptr(dy), _ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    return out
+
+
+def _act_quantize(name, fn, xs, fmt, scaling, layouts, out, stream):
+    L = lib()
+    _bf16_pair(name, *xs)
+    if xs[0].dim() != 2:
+        raise ValueError(name + ": tensors must be 2-D")
+    R, C = xs[0].shape
+    if out is None:
+        out = QTensor(R, C, scaling, _dev(xs[0]), row=bool(layouts & LAYOUT_ROW), col=bool(layouts & LAYOUT_COL))
+    wsb = L.fp8_quantize_workspace_bytes(R, C, scaling)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=xs[0].device)
+    oc = out.c()
+    _lib.check(fn(*[_ptr(t) for t in xs], R, C, fmt, scaling, layouts, ctypes.byref(oc), _ptr(ws), wsb,
+                  _stream(stream)))
+    return out
+
+
+def quantize_gelu(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None):
+    """Quantize GELU(x) without writing the activation (fp8_quantize_gelu);
+    tensorwise or 1x128 scaling."""
+    return _act_quantize("quantize_gelu", lib().fp8_quantize_gelu, (x,), fmt, scaling, layouts, out, stream)
+
+
+def quantize_dgelu(dy, x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None):
+    """Quantize dy * GELU'(x) without writing it (fp8_quantize_dgelu)."""
+    return _act_quantize("quantize_dgelu", lib().fp8_quantize_dgelu, (dy, x), fmt, scaling, layouts, out, stream)
+
+
 def gemm_scale(sinv, group=0, stride_r=0, stride_kb=0):
     """Scale descriptor of a GEMM operand; keeps a reference to the tensor so
     the device memory stays alive as long as the descriptor does."""
@@ -225,35 +279,56 @@ class Fp8Linear:
         self.ws, self.ws_bytes = linear_workspace(N, K, M, recipe, device)
         self._sx, self._dq, self._wq = self.saved_x.c(), self.dy_q.c(), self.w_q.c()
 
-    def forward(self, x, w, y=None, is_first_microbatch=None, stream=None, x_amax=None, y_amax=None):
+    def forward(self, x, w, y=None, is_first_microbatch=None, stream=None, x_amax=None, y_amax=None, gelu=False):
         """x_amax: X's amax partials from its producer (skips X's amax pass);
-        y_amax: receives Y's partials (tensorwise recipe)."""
+        y_amax: receives Y's partials (tensorwise recipe).  gelu=True: x is
+        the pre-activation and the layer's input is GELU(x), applied by X's
+        quantize (fp8_linear_fwd_gelu; no x_amax)."""
         flag = -1 if is_first_microbatch is None else int(bool(is_first_microbatch))
         if y is None:
             y = torch.empty((self.N, self.M), dtype=torch.bfloat16, device=x.device)
         cache = self.cache.handle if (self.cache is not None and flag != -1) else None
-        _lib.check(lib().fp8_linear_fwd(_ptr(x), _ptr(w), self.N, self.K, self.M, self.recipe, cache, flag,
-                                        _ptr(y), ctypes.byref(self._sx), ctypes.byref(self._wq),
-                                        _ptr(x_amax), _ptr(y_amax), _ptr(self.ws), self.ws_bytes,
-                                        _stream(stream)))
+        if gelu:
+            if x_amax is not None:
+                raise ValueError("no X amax hand-off with the GELU input")
+            _lib.check(lib().fp8_linear_fwd_gelu(_ptr(x), _ptr(w), self.N, self.K, self.M, self.recipe, cache, flag,
+                                                 _ptr(y), ctypes.byref(self._sx), ctypes.byref(self._wq),
+                                                 _ptr(y_amax), _ptr(self.ws), self.ws_bytes, _stream(stream)))
+        else:
+            _lib.check(lib().fp8_linear_fwd(_ptr(x), _ptr(w), self.N, self.K, self.M, self.recipe, cache, flag,
+                                            _ptr(y), ctypes.byref(self._sx), ctypes.byref(self._wq),
+                                            _ptr(x_amax), _ptr(y_amax), _ptr(self.ws), self.ws_bytes,
+                                            _stream(stream)))
         self._last_flag = flag
         return y
 
     def backward(self, dy, dx=None, dw=None, need_dx=True, need_dw=True, stream=None, dy_amax=None,
-                 dx_amax=None):
+                 dx_amax=None, gelu_input=None):
         """dy_amax: dY's amax partials from its producer (skips dY's amax
-        pass); dx_amax: receives dX's partials (tensorwise recipe)."""
+        pass); dx_amax: receives dX's partials (tensorwise recipe).
+        gelu_input: GELU's input (this layer's forward output); dy is then the
+        gradient of GELU's output and the incoming gradient is
+        dy * GELU'(gelu_input), applied by dY's quantize
+        (fp8_linear_bwd_dgelu; no dy_amax)."""
         if need_dx and dx is None:
             dx = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dy.device)
         if need_dw and dw is None:
             dw = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dy.device)
         use_cache = self.cache is not None and getattr(self, "_last_flag", -1) != -1
-        _lib.check(lib().fp8_linear_bwd(_ptr(dy), self.N, self.K, self.M, self.recipe,
-                                        ctypes.byref(self._sx), self.cache.handle if use_cache else None,
-                                        ctypes.byref(self._wq), ctypes.byref(self._dq),
-                                        _ptr(dx) if need_dx else None, _ptr(dw) if need_dw else None,
-                                        _ptr(dy_amax), _ptr(dx_amax), _ptr(self.ws), self.ws_bytes,
-                                        _stream(stream)))
+        cache = self.cache.handle if use_cache else None
+        dxp, dwp = (_ptr(dx) if need_dx else None), (_ptr(dw) if need_dw else None)
+        if gelu_input is not None:
+            if dy_amax is not None:
+                raise ValueError("no dY amax hand-off through GELU")
+            _lib.check(lib().fp8_linear_bwd_dgelu(_ptr(dy), _ptr(gelu_input), self.N, self.K, self.M, self.recipe,
+                                                  ctypes.byref(self._sx), cache, ctypes.byref(self._wq),
+                                                  ctypes.byref(self._dq), dxp, dwp, _ptr(dx_amax), _ptr(self.ws),
+                                                  self.ws_bytes, _stream(stream)))
+        else:
+            _lib.check(lib().fp8_linear_bwd(_ptr(dy), self.N, self.K, self.M, self.recipe,
+                                            ctypes.byref(self._sx), cache, ctypes.byref(self._wq),
+                                            ctypes.byref(self._dq), dxp, dwp, _ptr(dy_amax), _ptr(dx_amax),
+                                            _ptr(self.ws), self.ws_bytes, _stream(stream)))
         return dx, dw
 
     def weight_q(self):

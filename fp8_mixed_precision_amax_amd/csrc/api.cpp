@@ -109,8 +109,10 @@ fp8_status hip_status(hipError_t e, const char* what) {
 
 // given_amax: tensorwise only, the amax partials of x from its producer (the
 // amax pass is skipped); otherwise ws holds the pass's partials
+// act: 0 quantize x; 1 quantize GELU(x); 2 quantize dGELU(x, x2)
 fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, int scaling, unsigned layouts,
-                       const fp8_qtensor* out, void* ws, hipStream_t st, const void* given_amax = nullptr) {
+                       const fp8_qtensor* out, void* ws, hipStream_t st, const void* given_amax = nullptr,
+                       int act = 0, const void* x2 = nullptr) {
     fp8k::QuantizeLaunch q;
     q.x = x;
     q.rows = rows;
@@ -128,6 +130,8 @@ fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, in
     q.partial_given = given_amax != nullptr;
     q.hist = nullptr;
     q.hist_len = 0;
+    q.act = act;
+    q.x2 = x2;
     return hip_status(fp8k::launch_quantize(q, st), "quantize launch");
 }
 
@@ -265,6 +269,50 @@ fp8_status fp8_quantize_delayed(const void* x, int64_t rows, int64_t cols, fp8_f
     return hip_status(fp8k::launch_quantize(q, static_cast<hipStream_t>(stream)), "quantize launch");
 }
 
+fp8_status fp8_gelu(const void* x, void* y, int64_t n, void* stream) {
+    if (n < 0 || n % 8 != 0) return fail(FP8_ERR_SHAPE, "gelu: n = %lld must be a multiple of 8", (long long)n);
+    FP8_TRY(check_ptr16("x", x));
+    FP8_TRY(check_ptr16("y", y));
+    return hip_status(fp8k::launch_gelu(x, y, n, static_cast<hipStream_t>(stream)), "gelu launch");
+}
+
+fp8_status fp8_dgelu(const void* dy, const void* x, void* dx, int64_t n, void* stream) {
+    if (n < 0 || n % 8 != 0) return fail(FP8_ERR_SHAPE, "dgelu: n = %lld must be a multiple of 8", (long long)n);
+    FP8_TRY(check_ptr16("dy", dy));
+    FP8_TRY(check_ptr16("x", x));
+    FP8_TRY(check_ptr16("dx", dx));
+    return hip_status(fp8k::launch_dgelu(dy, x, dx, n, static_cast<hipStream_t>(stream)), "dgelu launch");
+}
+
+// Checks shared by the GELU-fused quantizers (tensorwise or 1x128 only).
+static fp8_status check_act_quantize(const void* x, int64_t rows, int64_t cols, int format, int scaling,
+                                     unsigned layouts, const fp8_qtensor* out, size_t ws_bytes, void* ws) {
+    if (scaling != FP8_SCALE_TENSOR && scaling != FP8_SCALE_BLOCK_1x128)
+        return fail(FP8_ERR_ENUM, "the GELU-fused quantizers take tensorwise or 1x128 scaling, not %d", scaling);
+    FP8_TRY(check_quantize(x, rows, cols, format, scaling, layouts, out));
+    const size_t need = fp8_quantize_workspace_bytes(rows, cols, static_cast<fp8_scaling>(scaling));
+    if (need) {
+        if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+        FP8_TRY(check_ptr16("ws", ws));
+    }
+    return FP8_OK;
+}
+
+fp8_status fp8_quantize_gelu(const void* x, int64_t rows, int64_t cols, fp8_format format, fp8_scaling scaling,
+                             unsigned layouts, const fp8_qtensor* out, void* ws, size_t ws_bytes, void* stream) {
+    FP8_TRY(check_act_quantize(x, rows, cols, format, scaling, layouts, out, ws_bytes, ws));
+    return do_quantize(x, rows, cols, format, scaling, layouts, out, ws, static_cast<hipStream_t>(stream), nullptr, 1);
+}
+
+fp8_status fp8_quantize_dgelu(const void* dy, const void* x, int64_t rows, int64_t cols, fp8_format format,
+                              fp8_scaling scaling, unsigned layouts, const fp8_qtensor* out, void* ws,
+                              size_t ws_bytes, void* stream) {
+    FP8_TRY(check_act_quantize(dy, rows, cols, format, scaling, layouts, out, ws_bytes, ws));
+    FP8_TRY(check_ptr16("x", x));
+    return do_quantize(dy, rows, cols, format, scaling, layouts, out, ws, static_cast<hipStream_t>(stream), nullptr, 2,
+                       x);
+}
+
 size_t fp8_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K) { return fp8k::gemm_ws_bytes(I, J, K); }
 
 static fp8_status gemm_checked(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb,
@@ -373,18 +421,20 @@ static fp8_status check_amax_handoff(int recipe, const void* in, const void* out
     return FP8_OK;
 }
 
-fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
-                          fp8_wcache cache, int flag, void* y, const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
-                          const void* x_amax_partials, void* y_amax_partials, void* ws, size_t ws_bytes,
-                          void* stream) {
+// act 1: the linear's input is GELU(x) (x the pre-activation), quantized
+// without being written out
+static fp8_status linear_fwd(const void* x, int act, const void* w, int64_t N, int64_t K, int64_t M,
+                             fp8_recipe recipe, fp8_wcache cache, int flag, void* y, const fp8_qtensor* saved_x,
+                             const fp8_qtensor* w_q, const void* x_amax_partials, void* y_amax_partials, void* ws,
+                             size_t ws_bytes, void* stream) {
     FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes));
     if (flag != -1 && flag != 0 && flag != 1) return fail(FP8_ERR_ENUM, "is_first_microbatch must be -1, 0 or 1");
     FP8_TRY(check_ptr16("x", x));
     FP8_TRY(check_ptr16("y", y));
     FP8_TRY(check_amax_handoff(recipe, x_amax_partials, y_amax_partials, "x_amax_partials", "y_amax_partials"));
-    const int act = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
+    const int xsc = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
     const int wsc = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_128x128 : FP8_SCALE_TENSOR;
-    FP8_TRY(check_quantize(x, N, K, FP8_E4M3, act, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x));
+    FP8_TRY(check_quantize(x, N, K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x));
     const fp8_qtensor* wq = nullptr;
     if (flag == -1) {
         FP8_TRY(check_weight_q(w_q, recipe, true, true));
@@ -410,7 +460,8 @@ fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, in
             cache->fills++;
         }
     }
-    FP8_TRY(do_quantize(x, N, K, FP8_E4M3, act, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x, ws, st, x_amax_partials));
+    FP8_TRY(do_quantize(x, N, K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x, ws, st, x_amax_partials,
+                        act));
     if (recipe == FP8_RECIPE_TENSOR)
         return do_gemm(saved_x->q_row, FP8_E4M3, tensor_scale(saved_x->scale_inv), wq->q_row, FP8_E4M3,
                        tensor_scale(wq->scale_inv), N, M, K, y, gws, gws_bytes, st, y_amax_partials);
@@ -418,10 +469,29 @@ fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, in
                    block_scale(wq->scale_inv, 128, K / 128, 1), N, M, K, y, gws, gws_bytes, st);
 }
 
-fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
-                          const fp8_qtensor* saved_x, fp8_wcache cache, const fp8_qtensor* w_q,
-                          const fp8_qtensor* dy_q, void* dx, void* dw, const void* dy_amax_partials,
-                          void* dx_amax_partials, void* ws, size_t ws_bytes, void* stream) {
+fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                          fp8_wcache cache, int flag, void* y, const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
+                          const void* x_amax_partials, void* y_amax_partials, void* ws, size_t ws_bytes,
+                          void* stream) {
+    return linear_fwd(x, 0, w, N, K, M, recipe, cache, flag, y, saved_x, w_q, x_amax_partials, y_amax_partials, ws,
+                      ws_bytes, stream);
+}
+
+fp8_status fp8_linear_fwd_gelu(const void* x_pre, const void* w, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                               fp8_wcache cache, int flag, void* y, const fp8_qtensor* saved_x,
+                               const fp8_qtensor* w_q, void* y_amax_partials, void* ws, size_t ws_bytes,
+                               void* stream) {
+    return linear_fwd(x_pre, 1, w, N, K, M, recipe, cache, flag, y, saved_x, w_q, nullptr, y_amax_partials, ws,
+                      ws_bytes, stream);
+}
+
+// act 2: the incoming gradient is dGELU(dy, y_pre): dy the gradient of
+// GELU's output and y_pre its input (this linear's output in the forward
+// pass), quantized without being written out
+static fp8_status linear_bwd(const void* dy, int act, const void* y_pre, int64_t N, int64_t K, int64_t M,
+                             fp8_recipe recipe, const fp8_qtensor* saved_x, fp8_wcache cache, const fp8_qtensor* w_q,
+                             const fp8_qtensor* dy_q, void* dx, void* dw, const void* dy_amax_partials,
+                             void* dx_amax_partials, void* ws, size_t ws_bytes, void* stream) {
     FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes));
     FP8_TRY(check_ptr16("dy", dy));
     if (!dx && !dw) return fail(FP8_ERR_NULL, "both dx and dw are NULL: nothing to compute");
@@ -429,9 +499,10 @@ fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_r
     if (dx_amax_partials && !dx) return fail(FP8_ERR_NULL, "dx_amax_partials given without dx");
     if (dx) FP8_TRY(check_ptr16("dx", dx));
     if (dw) FP8_TRY(check_ptr16("dw", dw));
-    const int act = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
+    const int gsc = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
     const unsigned lay = (dx ? FP8_LAYOUT_ROW : 0u) | (dw ? FP8_LAYOUT_COL : 0u);
-    FP8_TRY(check_quantize(dy, N, M, FP8_E5M2, act, lay, dy_q));
+    FP8_TRY(check_quantize(dy, N, M, FP8_E5M2, gsc, lay, dy_q));
+    if (act == 2) FP8_TRY(check_ptr16("y_pre", y_pre));
     const fp8_qtensor* wq = nullptr;
     if (dx) {
         if (cache) {
@@ -453,7 +524,7 @@ fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_r
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     void* gws = wsb + kPartialBytes;
     const size_t gws_bytes = ws_bytes - kPartialBytes;
-    FP8_TRY(do_quantize(dy, N, M, FP8_E5M2, act, lay, dy_q, ws, st, dy_amax_partials));
+    FP8_TRY(do_quantize(dy, N, M, FP8_E5M2, gsc, lay, dy_q, ws, st, dy_amax_partials, act, y_pre));
     if (dx) {
         if (recipe == FP8_RECIPE_TENSOR)
             FP8_TRY(do_gemm(dy_q->q_row, FP8_E5M2, tensor_scale(dy_q->scale_inv), wq->q_col, FP8_E4M3,
@@ -472,6 +543,22 @@ fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_r
                             st));
     }
     return FP8_OK;
+}
+
+fp8_status fp8_linear_bwd(const void* dy, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                          const fp8_qtensor* saved_x, fp8_wcache cache, const fp8_qtensor* w_q,
+                          const fp8_qtensor* dy_q, void* dx, void* dw, const void* dy_amax_partials,
+                          void* dx_amax_partials, void* ws, size_t ws_bytes, void* stream) {
+    return linear_bwd(dy, 0, nullptr, N, K, M, recipe, saved_x, cache, w_q, dy_q, dx, dw, dy_amax_partials,
+                      dx_amax_partials, ws, ws_bytes, stream);
+}
+
+fp8_status fp8_linear_bwd_dgelu(const void* dh, const void* y_pre, int64_t N, int64_t K, int64_t M,
+                                fp8_recipe recipe, const fp8_qtensor* saved_x, fp8_wcache cache,
+                                const fp8_qtensor* w_q, const fp8_qtensor* dy_q, void* dx, void* dw,
+                                void* dx_amax_partials, void* ws, size_t ws_bytes, void* stream) {
+    return linear_bwd(dh, 2, y_pre, N, K, M, recipe, saved_x, cache, w_q, dy_q, dx, dw, nullptr, dx_amax_partials,
+                      ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -27,10 +27,24 @@ struct QuantizeLaunch {
                         // the producer of x); the amax pass is skipped
     float* hist;        // delayed: amax history [hist_len], most recent first (read, then rolled);
     int hist_len;       // partial then holds one 16-bit amax per 128x128 tile
+    int act = 0;        // 0: quantize x; 1: quantize GELU(x); 2: quantize dGELU(x, x2), x the
+                        // gradient of GELU's output and x2 its input (scaling 0 or 1 only)
+    const void* x2 = nullptr;
 };
 
 int amax_partial_count(int64_t numel);
 hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream);
+
+// GELU tables of the current device (gelu.hip): built on first use, which
+// waits for them and cannot be captured into a graph.
+struct ActTables {
+    const uint16_t* gelu;   // bf16 GELU of the table's inputs
+    const float* dgelu;     // fp32 GELU' of the table's inputs
+};
+hipError_t act_tables(hipStream_t stream, ActTables& out);
+// elementwise GELU / dGELU over n bf16 values (n a multiple of 8)
+hipError_t launch_gelu(const void* x, void* y, int64_t n, hipStream_t stream);
+hipError_t launch_dgelu(const void* dy, const void* x, void* dx, int64_t n, hipStream_t stream);
 
 struct GemmScale {
     const float* sinv;

@@ -29,6 +29,16 @@
 //            rows with two xor shuffles.  The column layout is requantized
 //            with the column-block scales.
 //     MODE 2 128x128 blocks: one scale per tile (wave-wide reduction).
+//     MODE 3 tensorwise, delayed: the scale from an amax history; per-tile
+//            amaxes for history_update_kernel.
+//   act_amax_kernel<ACT>, act_cast_kernel<FMT,MODE,ACT>
+//                         the same passes on GELU(x) (ACT 1) or on
+//                         dy * GELU'(x) (ACT 2), the activation between the
+//                         two linears of an MLP block, computed from LDS
+//                         tables as the data arrives (act.hpp) and never
+//                         written out: each workgroup copies its table to
+//                         LDS once and then loops over tiles.
+#include "act.hpp"
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -41,14 +51,9 @@ constexpr int kAmaxThreads = 256;
 // recently read data while it is still in the memory-side cache.  Partial
 // maxima are bf16 magnitude bits (16 bits); workgroup 0 zero-fills the
 // unused tail of the kMaxAmaxPartials slots so readers may scan all of them.
-__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
-                                                                    uint16_t* __restrict__ partial) {
-    uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n16; i += stride) {
-        const uint4 v = x[i];
-        m = pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v.x), mag2(v.y)), pkmax_u16(mag2(v.z), mag2(v.w))));
-    }
+// The workgroup's maximum of the threads' packed magnitude maxima m goes to
+// partial[blockIdx.x]; workgroup 0 zero-fills the unused slots.
+__device__ __forceinline__ void amax_store_partial(uint32_t m, uint16_t* __restrict__ partial) {
     m = wave_max_u32(hmax_u16(m));
     __shared__ uint32_t red[kAmaxThreads / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -60,6 +65,54 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4*
     }
     if (blockIdx.x == 0)
         for (int p = (int)gridDim.x + threadIdx.x; p < kMaxAmaxPartials; p += kAmaxThreads) partial[p] = 0;
+}
+
+__device__ __forceinline__ uint32_t mag8_max(uint32_t m, uint4 v) {
+    return pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v.x), mag2(v.y)), pkmax_u16(mag2(v.z), mag2(v.w))));
+}
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                                    uint16_t* __restrict__ partial) {
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n16; i += stride) m = mag8_max(m, x[i]);
+    amax_store_partial(m, partial);
+}
+
+// Table bytes of an activation: the bf16 GELU table (ACT 1) or the fp32 GELU'
+// table (ACT 2).
+template <int ACT> constexpr uint32_t act_table_bytes() { return ACT == 2 ? kActEntries * 4 : kActEntries * 2; }
+
+// amax of GELU(x) (ACT 1) or of dGELU(x, x2) (ACT 2): the transform is
+// applied as in the cast, so both passes see the same bf16 values.
+template <int ACT>
+__global__ __launch_bounds__(kAmaxThreads) void act_amax_kernel(const uint4* __restrict__ x,
+                                                                const uint4* __restrict__ x2, int64_t n16,
+                                                                uint16_t* __restrict__ partial, const void* gtab) {
+    __shared__ __align__(16) uint32_t tab[act_table_bytes<ACT>() / 4];
+    act_table_to_lds(tab, gtab, sizeof(tab));
+    __syncthreads();
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        uint4 v[4], u[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            v[k] = ld_nt16(x + i + k * stride);
+            if constexpr (ACT == 2) u[k] = ld_nt16(x2 + i + k * stride);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            m = mag8_max(m, ACT == 1 ? gelu8(v[k], reinterpret_cast<const uint16_t*>(tab))
+                                     : dgelu8(v[k], u[k], reinterpret_cast<const float*>(tab)));
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = ld_nt16(x + i);
+        m = mag8_max(m, ACT == 1 ? gelu8(v, reinterpret_cast<const uint16_t*>(tab))
+                                 : dgelu8(v, ld_nt16(x2 + i), reinterpret_cast<const float*>(tab)));
+    }
+    amax_store_partial(m, partial);
 }
 
 struct CastArgs {
@@ -76,26 +129,33 @@ struct CastArgs {
     const float* hist;        // delayed only: amax history [hist_len]
     int hist_len;
     uint16_t* tile_amax;      // delayed only: amax of each 128x128 tile (bf16 magnitude bits)
+    const uint16_t* x2;       // dGELU only: GELU's input [R, C]; x is the gradient of its output
+    const void* act_tab;      // GELU / GELU' table (global memory), act_cast_kernel only
 };
 
-template <int FMT, int MODE>
-__global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+// One 128x128 tile, by one wave.  slot < number of tiles.  ACT 1 / 2 encode
+// GELU(x) / dGELU(x, x2) instead of x (tab: the table in LDS).
+template <int FMT, int MODE, int ACT>
+__device__ __forceinline__ void cast_tile(const CastArgs& a, int64_t slot, const void* tab) {
+    // lane, rowA and col0 are made opaque: in a loop over tiles the
+    // compiler would otherwise hoist everything derived from the lane (row
+    // offsets, shuffle addresses, lane masks) out of the loop, each value
+    // holding a register for the whole kernel
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
     const int64_t tiles_c = a.C >> 7;
     const int64_t ntiles = (a.R >> 7) * tiles_c;
     // tensorwise: last tile first (the amax pass swept front to back, so the
     // tail of the tensor is the part most likely still cached)
-    const int64_t slot = (int64_t)blockIdx.x * 4 + wave;
-    if (slot >= ntiles) return;
     const int64_t tile = MODE == 0 ? ntiles - 1 - slot : slot;
     const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
     const int rb = lane >> 4, cb = lane & 15;
     // this lane's rows: i < 16 -> rowA + i, i >= 16 -> rowB + (i - 16)
-    const int64_t rowA = tr * 128 + rb * 16;
+    int64_t rowA = tr * 128 + rb * 16;
+    int64_t col0 = tc * 128 + cb * 8;    // first of this lane's 8 columns
+    asm volatile("" : "+v"(rowA), "+v"(col0));
     const int64_t rowB = rowA + 64;
 #define FP8K_ROW(i) ((i) < 16 ? rowA + (i) : rowB + ((i) - 16))
-    const int64_t col0 = tc * 128 + cb * 8;    // first of this lane's 8 columns
 
     // tensorwise: the amax partials (issued first, they return first)
     uint4 pw[kMaxAmaxPartials / 512];
@@ -116,8 +176,59 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
 
     // ---- load 32 rows x 8 bf16 ------------------------------------------
     uint4 v[32];
+    if constexpr (ACT == 2) {
+        // the gradient and GELU's input, 16 rows at a time (all 32 rows of
+        // both would need every register of the wave)
+        const float* t = static_cast<const float*>(tab);
+        us2_t far = {0, 0};
+        uint32_t dm = 0;
 #pragma unroll
-    for (int i = 0; i < 32; i++) v[i] = ld_nt16(a.x + FP8K_ROW(i) * a.C + col0);
+        for (int hf = 0; hf < 2; hf++) {
+            uint4 u[16];
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                v[16 * hf + i] = ld_nt16(a.x + FP8K_ROW(16 * hf + i) * a.C + col0);
+                u[i] = ld_nt16(a.x2 + FP8K_ROW(16 * hf + i) * a.C + col0);
+            }
+            // 4 rows between scheduling barriers: otherwise every table read
+            // of the tile is hoisted to the top, each holding a register
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                v[16 * hf + i] = dgelu8_fast(v[16 * hf + i], u[i], t, far, dm);
+                if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // a tile with an input outside the table or a non-finite gradient:
+        // read it again and take the exact path, 4 rows at a time
+        if (act_need_full(far, dm)) {
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                v[i] = dgelu8_full(ld_nt16(a.x + FP8K_ROW(i) * a.C + col0), ld_nt16(a.x2 + FP8K_ROW(i) * a.C + col0), t);
+                if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; i++) v[i] = ld_nt16(a.x + FP8K_ROW(i) * a.C + col0);
+        if constexpr (ACT == 1) {
+            const uint16_t* t = static_cast<const uint16_t*>(tab);
+            us2_t far = {0, 0};
+            // 4 rows between scheduling barriers: otherwise every table read
+            // of the tile is hoisted to the top, each holding a register
+#pragma unroll
+            for (int i = 0; i < 32; i++) {
+                v[i] = gelu8_fast(v[i], t, far);
+                if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            if (act_need_full(far)) {
+#pragma unroll
+                for (int i = 0; i < 32; i++) {
+                    v[i] = gelu8_full(ld_nt16(a.x + FP8K_ROW(i) * a.C + col0), t);
+                    if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
 
     // ---- scales ---------------------------------------------------------
     float s_tile = 1.0f;          // MODE 0, 2 and 3
@@ -315,6 +426,32 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
 #undef FP8K_ROW
 }
 
+template <int FMT, int MODE>
+__global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
+    const int64_t ntiles = (a.R >> 7) * (a.C >> 7);
+    const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (slot >= ntiles) return;
+    cast_tile<FMT, MODE, 0>(a, slot, nullptr);
+}
+
+// MODE 0 or 1 on GELU(x) / dGELU(x, x2): the table goes to LDS once per
+// workgroup.  Tensorwise, the workgroup's waves then take tiles in turn; in
+// 1x128 blocks each wave takes one tile (in a loop the compiler interleaves
+// the row- and column-block parts and needs twice the registers).
+template <int FMT, int MODE, int ACT>
+__global__ __launch_bounds__(256) void act_cast_kernel(CastArgs a) {
+    __shared__ __align__(16) uint32_t tab[act_table_bytes<ACT>() / 4];
+    act_table_to_lds(tab, a.act_tab, sizeof(tab));
+    __syncthreads();
+    const int64_t ntiles = (a.R >> 7) * (a.C >> 7);
+    const int64_t slot0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if constexpr (MODE == 1) {
+        if (slot0 < ntiles) cast_tile<FMT, MODE, ACT>(a, slot0, tab);
+    } else {
+        for (int64_t slot = slot0; slot < ntiles; slot += (int64_t)gridDim.x * 4) cast_tile<FMT, MODE, ACT>(a, slot, tab);
+    }
+}
+
 // Delayed scaling, after the cast: this call's amax from the per-tile maxima,
 // then the history rolls by one (oldest entry dropped) and takes it in front.
 __global__ __launch_bounds__(256) void history_update_kernel(const uint16_t* __restrict__ tile_amax, int64_t ntiles,
@@ -355,6 +492,48 @@ int amax_partial_count(int64_t numel) {
     return (int)g;
 }
 
+// Quantize GELU(x) (q.act 1) or dGELU(x, x2) (q.act 2), tensorwise (two
+// passes) or in 1x128 blocks (one pass).
+hipError_t launch_act_quantize(const QuantizeLaunch& q, CastArgs& a, hipStream_t stream) {
+    ActTables t;
+    hipError_t e = act_tables(stream, t);
+    if (e != hipSuccess) return e;
+    a.act_tab = q.act == 1 ? static_cast<const void*>(t.gelu) : static_cast<const void*>(t.dgelu);
+    if (q.scaling == 0) {
+        // about two workgroups per CU: each one copies the table to LDS first
+        const int64_t n16 = q.rows * q.cols / 8;
+        int64_t g = (n16 + (int64_t)kAmaxThreads * 16 - 1) / ((int64_t)kAmaxThreads * 16);
+        g = g < 1 ? 1 : (g > 512 ? 512 : g);
+        if (q.act == 1)
+            hipLaunchKernelGGL(act_amax_kernel<1>, dim3((unsigned)g), dim3(kAmaxThreads), 0, stream,
+                               static_cast<const uint4*>(q.x), nullptr, n16, q.partial, a.act_tab);
+        else
+            hipLaunchKernelGGL(act_amax_kernel<2>, dim3((unsigned)g), dim3(kAmaxThreads), 0, stream,
+                               static_cast<const uint4*>(q.x), static_cast<const uint4*>(q.x2), n16, q.partial,
+                               a.act_tab);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // tensorwise: two workgroups per CU (the transform's registers allow two
+    // waves per SIMD), each looping over tiles; 1x128: one tile per wave
+    const int64_t ntiles = (q.rows / 128) * (q.cols / 128);
+    int64_t g = (ntiles + 3) / 4;
+    if (q.scaling == 0 && g > 512) g = 512;
+    const dim3 grid((unsigned)g);
+#define FP8K_ACT(F, M, A) hipLaunchKernelGGL((act_cast_kernel<F, M, A>), grid, dim3(256), 0, stream, a)
+#define FP8K_ACT_F(M, A) \
+    if (q.format == 0) FP8K_ACT(0, M, A); \
+    else FP8K_ACT(1, M, A)
+    if (q.scaling == 0) {
+        if (q.act == 1) { FP8K_ACT_F(0, 1); } else { FP8K_ACT_F(0, 2); }
+    } else {
+        if (q.act == 1) { FP8K_ACT_F(1, 1); } else { FP8K_ACT_F(1, 2); }
+    }
+#undef FP8K_ACT_F
+#undef FP8K_ACT
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     CastArgs a;
     a.x = static_cast<const uint16_t*>(q.x);
@@ -371,6 +550,9 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     a.hist = q.hist;
     a.hist_len = q.hist_len;
     a.tile_amax = q.partial;
+    a.x2 = static_cast<const uint16_t*>(q.x2);
+    a.act_tab = nullptr;
+    if (q.act) return launch_act_quantize(q, a, stream);
     if (q.scaling == 0 && !q.partial_given) {
         const int g = amax_partial_count(q.rows * q.cols);
         hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(kAmaxThreads), 0, stream,

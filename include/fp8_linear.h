@@ -306,6 +306,81 @@ fp8_status fp8_linear_bwd(const void* dy_bf16, int64_t N, int64_t K, int64_t M, 
                           const void* dy_amax_partials, void* dx_amax_partials,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* ----------------------- GELU in an MLP block ------------------------ */
+
+/*
+ * The MLP block of the pages' workload (512 -> 2048 -> 512 linears with GELU
+ * between them, as in "Native FP8 MLP reconstruction", where the MLP linears
+ * are the ones run in FP8) needs GELU on the up projection's output and
+ * GELU's derivative on the way back.  The exact (erf) form is used:
+ *   GELU(x) = x Phi(x),  GELU'(x) = Phi(x) + x phi(x)
+ * (Phi, phi the standard normal CDF and density), each rounded once to fp32
+ * from an fp64 evaluation.  The activation is bf16(fl32(GELU(x))), the
+ * gradient through GELU bf16(fl32(dy * fl32(GELU'(x)))) (one fp32 multiply),
+ * both rounded to nearest even; every NaN result is the quiet NaN 0x7FC0
+ * (GELU(-Inf) = -Inf * 0 is one, so is GELU' of either infinity).
+ *
+ * The values come from tables of both functions over the bf16 inputs, built
+ * on each device the first time one of these functions runs there: that
+ * call waits for the tables (on a stream of its own) and fails with
+ * FP8_ERR_HIP if its stream is being captured into a graph.  Later calls
+ * enqueue only.
+ */
+
+/* y [n] = GELU(x [n]), bf16 in and out; n a multiple of 8 (FP8_ERR_SHAPE),
+ * pointers 16-byte aligned.  The unfused form, for comparison and for a
+ * caller that needs the activation in bf16. */
+fp8_status fp8_gelu(const void* x_bf16, void* y_bf16, int64_t n, void* stream);
+
+/* dx [n] = dGELU(dy [n], x [n]): dy the gradient of GELU's output, x GELU's
+ * input; bf16 in and out, n a multiple of 8. */
+fp8_status fp8_dgelu(const void* dy_bf16, const void* x_bf16, void* dx_bf16, int64_t n, void* stream);
+
+/*
+ * Quantize GELU(x) [rows, cols] exactly as fp8_quantize would quantize the
+ * bf16 activation, without writing the activation out: the bytes and scales
+ * are identical to fp8_gelu followed by fp8_quantize.  scaling is
+ * FP8_SCALE_TENSOR (two passes over x: amax, then the cast) or
+ * FP8_SCALE_BLOCK_1x128 (one pass); FP8_ERR_ENUM otherwise.  Workspace and
+ * the other arguments as fp8_quantize.
+ */
+fp8_status fp8_quantize_gelu(const void* x_bf16, int64_t rows, int64_t cols, fp8_format format,
+                             fp8_scaling scaling, unsigned layouts, const fp8_qtensor* out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Quantize dGELU(dy, x) [rows, cols] likewise (identical to fp8_dgelu
+ * followed by fp8_quantize); x is 16-byte aligned and has dy's shape. */
+fp8_status fp8_quantize_dgelu(const void* dy_bf16, const void* x_bf16, int64_t rows, int64_t cols,
+                              fp8_format format, fp8_scaling scaling, unsigned layouts,
+                              const fp8_qtensor* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The second linear of an MLP block: fp8_linear_fwd with X = GELU(x_pre),
+ * x_pre [N, K] the first linear's output.  X's quantize applies GELU as it
+ * reads x_pre; saved_x holds X's codes (and scales), exactly what
+ * fp8_linear_fwd gives for X = fp8_gelu(x_pre).  No X amax hand-off; the
+ * other arguments as fp8_linear_fwd.
+ */
+fp8_status fp8_linear_fwd_gelu(const void* x_pre_bf16, const void* w_bf16,
+                               int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                               fp8_wcache cache, int is_first_microbatch,
+                               void* y_bf16, const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
+                               void* y_amax_partials, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The first linear of an MLP block, backward: fp8_linear_bwd with the
+ * incoming gradient dY = dGELU(dh, y_pre), dh [N, M] the gradient of GELU's
+ * output and y_pre [N, M] GELU's input (this linear's forward output).  dY's
+ * quantize applies dGELU as it reads both; the results equal fp8_linear_bwd
+ * on dY = fp8_dgelu(dh, y_pre).  No dY amax hand-off; the other arguments as
+ * fp8_linear_bwd.
+ */
+fp8_status fp8_linear_bwd_dgelu(const void* dh_bf16, const void* y_pre_bf16, int64_t N, int64_t K,
+                                int64_t M, fp8_recipe recipe, const fp8_qtensor* saved_x,
+                                fp8_wcache cache, const fp8_qtensor* w_q, const fp8_qtensor* dy_q,
+                                void* dx_bf16, void* dw_bf16, void* dx_amax_partials,
+                                void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------- misc -------------------------------- */
 
 const char* fp8_status_string(fp8_status status);

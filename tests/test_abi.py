@@ -184,3 +184,43 @@ def test_cache_lifecycle_and_errors(L):
     assert L.fp8_wcache_valid(h) == 0          # nothing above filled it
     L.fp8_wcache_destroy(h)
     L.fp8_wcache_destroy(None)
+
+
+def test_gelu_argument_errors(L):
+    """GELU of the MLP block: elementwise ops, the fused quantizers and the
+    two MLP-block linears validate like the plain entry points."""
+    assert L.fp8_gelu(A, A, 12, None) == SHAPE
+    assert L.fp8_gelu(A, A, -8, None) == SHAPE
+    assert L.fp8_gelu(None, A, 8, None) == NULL
+    assert L.fp8_gelu(A, U, 8, None) == ALIGN
+    assert L.fp8_gelu(A, A, 0, None) == OK                 # empty: nothing is enqueued
+    assert L.fp8_dgelu(A, None, A, 8, None) == NULL
+    assert L.fp8_dgelu(A, A, U, 8, None) == ALIGN
+    assert L.fp8_dgelu(A, A, A, 4, None) == SHAPE
+    o = qt()
+
+    def qg(x=A, R=256, C=256, sc=0, ws=A, wsb=4096):
+        return L.fp8_quantize_gelu(x, R, C, 0, sc, 3, ctypes.byref(o), ws, wsb, None)
+
+    def qd(x=A, sc=0):
+        return L.fp8_quantize_dgelu(A, x, 256, 256, 1, sc, 3, ctypes.byref(o), A, 4096, None)
+
+    assert qg(sc=2) == ENUM                                # 128x128 blocks are for weights
+    assert qg(R=200) == SHAPE
+    assert qg(x=U) == ALIGN
+    assert qg(wsb=100) == WORKSPACE
+    assert qd(x=None) == NULL and qd(x=U) == ALIGN and qd(sc=2) == ENUM
+    wsb = L.fp8_linear_workspace_bytes(256, 256, 256, 0)
+    sx = qt()
+
+    def fwd(N=256, wq=True):
+        return L.fp8_linear_fwd_gelu(A, A, N, 256, 256, 0, None, -1, A, ctypes.byref(sx),
+                                     ctypes.byref(qt()) if wq else None, None, A, wsb, None)
+
+    def bwd(y_pre=A):
+        return L.fp8_linear_bwd_dgelu(A, y_pre, 256, 256, 256, 0, ctypes.byref(sx), None, ctypes.byref(qt()),
+                                      ctypes.byref(qt()), A, A, None, A, wsb, None)
+
+    assert fwd(N=200) == SHAPE
+    assert fwd(wq=False) == NULL                           # None (-1) needs w_q
+    assert bwd(y_pre=None) == NULL and bwd(y_pre=U) == ALIGN

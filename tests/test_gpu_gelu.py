@@ -1,0 +1,227 @@
+"""GELU between the two linears of the MLP block, on the GPU through the C ABI.
+
+Bit-exact against the oracle (exact erf GELU, fl32-rounded, bf16 outputs):
+  - fp8_gelu at every one of the 65536 bf16 inputs, in order and shuffled
+    (so table lookups and the closed forms meet within one wave);
+  - fp8_dgelu at every bf16 input with gradients from several distributions
+    (normal, subnormal, huge enough to overflow, +-0, +-Inf, NaN);
+  - fp8_quantize_gelu / fp8_quantize_dgelu (codes, scales, amax) on seeded
+    pre-activations shaped like the MLP block's, with and without planted
+    special values, tensorwise and in 1x128 blocks;
+  - the fused quantize against fp8_gelu / fp8_dgelu + fp8_quantize, bitwise,
+    at the full MLP-block size (131072 x 2048);
+  - the block's two linears layer by layer (fp8_linear_fwd_gelu,
+    fp8_linear_bwd_dgelu), the oracle fed the GPU's own bf16 layer inputs:
+    quantized bytes exact, GEMM outputs within the BF16 tolerance, and
+    bitwise equal to the unfused calls.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _util import check_bf16, mfma_window_bound, to_np_u16, to_np_u8
+
+pytestmark = pytest.mark.gpu
+
+FMT = {"e4m3": 0, "e5m2": 1}
+
+
+@pytest.fixture(scope="module")
+def fp8():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_mixed_precision_amax_amd as m
+    m.lib()
+    return m
+
+
+def _u16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _all_bf16():
+    return np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+@pytest.mark.parametrize("shuffled", [False, True])
+def test_gelu_every_bf16_input(fp8, shuffled):
+    x = _all_bf16()
+    if shuffled:
+        x = x[np.random.default_rng(1).permutation(x.size)]
+    print("gelu all inputs shuffled=%s" % shuffled, flush=True)
+    got = to_np_u16(fp8.gelu(_u16(x)))
+    ref = oracle.gelu(x)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(hex(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:8]]
+
+
+def test_dgelu_every_bf16_input(fp8):
+    rng = np.random.default_rng(2)
+    x = np.tile(_all_bf16(), 8)
+    rng.shuffle(x)
+    n = x.size
+    dy = np.empty(n, np.uint16)
+    k = n // 8
+    dy[:3 * k] = oracle.bf16_rne((rng.standard_normal(3 * k) * 1e-3).astype(np.float32))
+    dy[3 * k:4 * k] = oracle.bf16_rne((rng.standard_normal(k) * 3.0).astype(np.float32))
+    dy[4 * k:5 * k] = rng.integers(0, 0x80, k).astype(np.uint16) | (rng.integers(0, 2, k).astype(np.uint16) << 15)
+    # near the bf16 maximum: dy * GELU'(x) overflows to +-Inf where GELU'(x) > 1
+    dy[5 * k:6 * k] = oracle.bf16_rne(np.clip(rng.standard_normal(k) * 1e38, -3.3e38, 3.3e38).astype(np.float32))
+    dy[6 * k:] = rng.choice(np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0x3F80], np.uint16), n - 6 * k)
+    perm = rng.permutation(n)
+    dy = dy[perm]
+    print("dgelu", n, flush=True)
+    got = to_np_u16(fp8.dgelu(_u16(dy), _u16(x)))
+    ref = oracle.dgelu(dy, x)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(hex(dy[i]), hex(x[i]), hex(got[i]), hex(ref[i])) for i in bad[:8]]
+
+
+def _pre_activation(R, C, seed, special=False):
+    """Pre-activations as the MLP block's up projection gives them: X ~ N(0,1)
+    times W ~ N(0, 0.02) over K = 512 has sigma 0.02 * sqrt(512) ~ 0.45."""
+    g = torch.Generator().manual_seed(seed)
+    a = synth.bits(synth.normal_bf16((R, C), 0.45, g)).copy()
+    if special:
+        rng = np.random.default_rng(seed)
+        vals = np.array([0x0000, 0x8000, 0x0001, 0x8080, 0x2000, 0x4180, 0xC180, 0x4500, 0xC500,
+                         0x7F80, 0xFF80, 0x7FC0, 0x7F7F, 0xFF7F], np.uint16)
+        idx = rng.choice(a.size, 64, replace=False)
+        a.reshape(-1)[idx] = rng.choice(vals, idx.size)
+    return a
+
+
+def _check_q(q, ref, scaling):
+    assert np.array_equal(to_np_u8(q.q_row), ref["q_row"]), "q_row"
+    assert np.array_equal(to_np_u8(q.q_col), ref["q_col"]), "q_col"
+    f = lambda t: t.detach().cpu().numpy().view(np.uint32)
+    if scaling == "tensor":
+        assert f(q.scale)[0] == np.float32(ref["scale"]).view(np.uint32)
+        assert f(q.scale_inv)[0] == np.float32(ref["scale_inv"]).view(np.uint32)
+        assert f(q.amax)[0] == np.float32(ref["amax"]).view(np.uint32) or (
+            np.isnan(ref["amax"]) and np.isnan(q.amax.cpu().numpy()[0]))
+    else:
+        assert np.array_equal(f(q.scale), ref["scale_row"].view(np.uint32))
+        assert np.array_equal(f(q.scale_inv), ref["scale_inv_row"].view(np.uint32))
+        assert np.array_equal(f(q.scale_col), ref["scale_col"].view(np.uint32))
+        assert np.array_equal(f(q.scale_inv_col), ref["scale_inv_col"].view(np.uint32))
+
+
+QCASES = [
+    # R, C, special values planted
+    (256, 384, False),       # a few tiles, odd tile count per row
+    (640, 1024, False),      # ragged against the cast's 4-tile workgroups
+    (1024, 2048, True),      # the MLP block's hidden width, specials
+    (384, 256, True),
+]
+
+
+@pytest.mark.parametrize("scaling", ["tensor", "1x128"])
+@pytest.mark.parametrize("R,C,special", QCASES)
+def test_quantize_gelu_matches_oracle(fp8, R, C, special, scaling):
+    a = _pre_activation(R, C, 10 + R + C, special)
+    sc = fp8.SCALE_TENSOR if scaling == "tensor" else fp8.SCALE_1x128
+    print("quantize_gelu", R, C, special, scaling, flush=True)
+    q = fp8.quantize_gelu(_u16(a), fp8.E4M3, sc)
+    torch.cuda.synchronize()
+    _check_q(q, oracle.quant_gelu(a, "e4m3", scaling), scaling)
+
+
+@pytest.mark.parametrize("scaling", ["tensor", "1x128"])
+@pytest.mark.parametrize("R,C,special", QCASES)
+def test_quantize_dgelu_matches_oracle(fp8, R, C, special, scaling):
+    a = _pre_activation(R, C, 20 + R + C, special)
+    g = torch.Generator().manual_seed(30 + R)
+    dh = synth.bits(synth.normal_bf16((R, C), 1e-3, g)).copy()
+    if special:
+        dh.reshape(-1)[::997] = 0x7F80                   # +Inf gradients: NaN where GELU'(x) = 0
+    sc = fp8.SCALE_TENSOR if scaling == "tensor" else fp8.SCALE_1x128
+    print("quantize_dgelu", R, C, special, scaling, flush=True)
+    q = fp8.quantize_dgelu(_u16(dh), _u16(a), fp8.E5M2, sc)
+    torch.cuda.synchronize()
+    _check_q(q, oracle.quant_dgelu(dh, a, "e5m2", scaling), scaling)
+
+
+@pytest.mark.parametrize("scaling", ["tensor", "1x128"])
+def test_fused_equals_unfused_at_mlp_size(fp8, scaling):
+    """131072 x 2048, the MLP block's hidden activation: the fused quantize
+    gives the bytes and scales of GELU (or dGELU) followed by the quantize."""
+    R, C = 131072, 2048
+    print("fused vs unfused", R, C, scaling, flush=True)
+    g = torch.Generator(device="cuda").manual_seed(40)
+    a = synth.normal_bf16((R, C), 0.45, g, device="cuda")
+    dh = synth.normal_bf16((R, C), 1e-3, g, device="cuda")
+    sc = fp8.SCALE_TENSOR if scaling == "tensor" else fp8.SCALE_1x128
+    names = ["q_row", "q_col", "scale", "scale_inv"] + (["amax"] if scaling == "tensor" else
+                                                        ["scale_col", "scale_inv_col"])
+    fused = fp8.quantize_gelu(a, fp8.E4M3, sc)
+    plain = fp8.quantize(fp8.gelu(a), fp8.E4M3, sc)
+    torch.cuda.synchronize()
+    for n in names:
+        assert torch.equal(getattr(fused, n), getattr(plain, n)), ("gelu", n)
+    del fused, plain
+    fused = fp8.quantize_dgelu(dh, a, fp8.E5M2, sc)
+    plain = fp8.quantize(fp8.dgelu(dh, a), fp8.E5M2, sc)
+    torch.cuda.synchronize()
+    for n in names:
+        assert torch.equal(getattr(fused, n), getattr(plain, n)), ("dgelu", n)
+
+
+@pytest.mark.parametrize("recipe", ["tensor", "block"])
+def test_mlp_block_layers(fp8, recipe):
+    """One MLP block 512 -> 2048 -> 512 at N = 1024.  Layer by layer against
+    the oracle (fed the GPU's bf16 A and dH), and the fused entry points
+    bitwise equal to the unfused ones."""
+    N, d, h = 1024, 512, 2048
+    R = fp8.RECIPE_TENSOR if recipe == "tensor" else fp8.RECIPE_BLOCK
+    act = "tensor" if recipe == "tensor" else "1x128"
+    print("mlp block", N, d, h, recipe, flush=True)
+    g = torch.Generator().manual_seed(50)
+    x = synth.normal_bf16((N, d), 1.0, g)
+    w1 = synth.normal_bf16((h, d), 0.02, g)
+    w2 = synth.normal_bf16((d, h), 0.02, g)
+    dy = synth.normal_bf16((N, d), 1e-3, g)
+    l1, l2 = fp8.Fp8Linear(N, d, h, R), fp8.Fp8Linear(N, h, d, R)
+    a = l1.forward(x.cuda(), w1.cuda())
+    y = l2.forward(a, w2.cuda(), gelu=True)
+    dhid, dw2 = l2.backward(dy.cuda())
+    dx, dw1 = l1.backward(dhid, gelu_input=a)
+    torch.cuda.synchronize()
+    A, DH = to_np_u16(a), to_np_u16(dhid)
+
+    # the second linear, its input GELU(A)
+    yr, ctx2 = oracle.linear_fwd_gelu(A, synth.bits(w2), "tensor" if recipe == "tensor" else "block")
+    xq = ctx2["xq"]
+    _check_q(l2.saved_x, xq, act)
+    if recipe == "tensor":
+        t = np.float32(xq["scale_inv"] * ctx2["wq"]["scale_inv"])
+    else:
+        t = (xq["scale_inv_row"], np.repeat(ctx2["wq"]["scale_inv"], 128, axis=0))
+    check_bf16(to_np_u16(y), yr, h, "Y2", mfma_window_bound(xq["q_row"], "e4m3", ctx2["wq"]["q_row"], "e4m3", t))
+
+    # the first linear's backward, its incoming gradient dGELU(dH, A)
+    _, ctx1 = oracle.linear_fwd(synth.bits(x), synth.bits(w1), "tensor" if recipe == "tensor" else "block")
+    dxr, dw1r, dyq = oracle.linear_bwd_dgelu(DH, A, ctx1)
+    _check_q(l1.dy_q, dyq, act)
+    wq, xq1 = ctx1["wq"], ctx1["xq"]
+    if recipe == "tensor":
+        tdx = np.float32(dyq["scale_inv"] * wq["scale_inv"])
+        tdw = np.float32(dyq["scale_inv"] * xq1["scale_inv"])
+    else:
+        tdx = (dyq["scale_inv_row"], np.repeat(wq["scale_inv"].T, 128, axis=0))
+        tdw = (dyq["scale_inv_col"], xq1["scale_inv_col"])
+    check_bf16(to_np_u16(dx), dxr, h, "dX1", mfma_window_bound(dyq["q_row"], "e5m2", wq["q_col"], "e4m3", tdx))
+    check_bf16(to_np_u16(dw1), dw1r, N, "dW1", mfma_window_bound(dyq["q_col"], "e5m2", xq1["q_col"], "e4m3", tdw))
+
+    # the unfused calls give the same bits
+    u1, u2 = fp8.Fp8Linear(N, d, h, R), fp8.Fp8Linear(N, h, d, R)
+    ua = u1.forward(x.cuda(), w1.cuda())
+    uy = u2.forward(fp8.gelu(ua), w2.cuda())
+    udh, _ = u2.backward(dy.cuda())
+    udx, udw1 = u1.backward(fp8.dgelu(udh, ua))
+    torch.cuda.synchronize()
+    for n, p, q in (("Y2", y, uy), ("dX1", dx, udx), ("dW1", dw1, udw1)):
+        assert torch.equal(p.view(torch.int16), q.view(torch.int16)), n
+    assert torch.equal(l2.saved_x.q_col, u2.saved_x.q_col) and torch.equal(l1.dy_q.q_col, u1.dy_q.q_col)
