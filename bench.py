@@ -444,6 +444,85 @@ def delayed_quant_times(fp8, torch, synth, N, reps, dev):
             "ms_current": round(res["current"], 4), "gbs_current": round(6 * n / res["current"] / 1e6, 1)}
 
 
+def _ms(torch, fn, reps, warm=3):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def mlp_gelu_times(fp8, torch, synth, N, steps, warmup, reps, dev):
+    """GELU between the two linears (the MLP block 512 -> 2048 -> 512).
+    Quantize level, on the hidden activation [N, 2048]: GELU fused into the
+    second linear's X quantize against GELU written out in bf16 and then
+    quantized, and dGELU fused into the first linear's dY quantize against
+    the same two steps unfused.  Algorithmic bytes per element, tensorwise:
+    fused GELU 6 (x read twice, two codes), unfused 10 (+ the bf16
+    activation written and read); fused dGELU 10 (both inputs read twice),
+    unfused 12; 1x128 (one pass): fused 4 and 6.  Block level: one forward +
+    backward of the MLP block, fused entry points against unfused ones."""
+    (K1, M1), (K2, M2) = SHAPES
+    g = torch.Generator(device=dev).manual_seed(77)
+    a = synth.normal_bf16((N, M1), 0.45, g, device=dev)          # pre-activation, sigma 0.02 * sqrt(512)
+    dh = synth.normal_bf16((N, M1), 1e-3, g, device=dev)
+    n = N * M1
+    res = {"workload": "MLP block 512->2048 (GELU) ->512, N=%d; hidden activation %dx%d" % (N, N, M1)}
+    hbuf = torch.empty_like(a)
+    for scaling, sname in ((fp8.SCALE_TENSOR, "tensor"), (fp8.SCALE_1x128, "1x128")):
+        qx = fp8.QTensor(N, M1, scaling, dev)
+        qd = fp8.QTensor(N, M1, scaling, dev)
+        t = {
+            "gelu_fused": _ms(torch, lambda: fp8.quantize_gelu(a, fp8.E4M3, scaling, out=qx), reps),
+            "gelu_unfused": _ms(torch, lambda: fp8.quantize(fp8.gelu(a, out=hbuf), fp8.E4M3, scaling, out=qx), reps),
+            "dgelu_fused": _ms(torch, lambda: fp8.quantize_dgelu(dh, a, fp8.E5M2, scaling, out=qd), reps),
+            "dgelu_unfused": _ms(torch, lambda: fp8.quantize(fp8.dgelu(dh, a, out=hbuf), fp8.E5M2, scaling, out=qd),
+                                 reps),
+        }
+        one = sname == "1x128"
+        algo = {"gelu_fused": 4 if one else 6, "gelu_unfused": 8 if one else 10,
+                "dgelu_fused": 6 if one else 10, "dgelu_unfused": 10 if one else 12}
+        res[sname] = {k: {"ms": round(v, 4), "algorithmic_gbs": round(algo[k] * n / v / 1e6, 1),
+                          "hbm_frac": round(algo[k] * n / v / 1e6 / HBM_PEAK_GBS, 3)} for k, v in t.items()}
+        del qx, qd
+    del hbuf
+    # one forward + backward of the block, tensorwise
+    x, w1, _ = synth.operands_on_device(N, K1, M1, seed=0, device=dev)
+    _, w2, dy = synth.operands_on_device(N, K2, M2, seed=1, device=dev)
+    l1, l2 = fp8.Fp8Linear(N, K1, M1, device=dev), fp8.Fp8Linear(N, K2, M2, device=dev)
+    ya = torch.empty((N, M1), dtype=torch.bfloat16, device=dev)
+    h = torch.empty_like(ya)
+    dhid = torch.empty_like(ya)
+    y2 = torch.empty((N, M2), dtype=torch.bfloat16, device=dev)
+    dx1 = torch.empty((N, K1), dtype=torch.bfloat16, device=dev)
+    dw1 = torch.empty((M1, K1), dtype=torch.bfloat16, device=dev)
+    dw2 = torch.empty((M2, K2), dtype=torch.bfloat16, device=dev)
+
+    def fused():
+        l1.forward(x, w1, y=ya)
+        l2.forward(ya, w2, y=y2, gelu=True)
+        l2.backward(dy, dx=dhid, dw=dw2)
+        l1.backward(dhid, dx=dx1, dw=dw1, gelu_input=ya)
+
+    def unfused():
+        l1.forward(x, w1, y=ya)
+        l2.forward(fp8.gelu(ya, out=h), w2, y=y2)
+        l2.backward(dy, dx=dhid, dw=dw2)
+        l1.backward(fp8.dgelu(dhid, ya, out=h), dx=dx1, dw=dw1)
+
+    flops = sum(6 * N * K * M for K, M in SHAPES)
+    bf, bu = _ms(torch, fused, steps, warmup), _ms(torch, unfused, steps, warmup)
+    res["block"] = {"ms_fused": round(bf, 4), "ms_unfused": round(bu, 4),
+                    "tflops_fused": round(flops / (bf / 1e3) / 1e12, 2),
+                    "tflops_unfused": round(flops / (bu / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
+    return res
+
+
 def measured_traffic(stage):
     """HBM bytes per launch of `stage` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE scaled by the copy calibration), or None when
@@ -579,6 +658,12 @@ def main():
         delayed = delayed_quant_times(fp8, torch, synth, N, args.reps, dev)
         print("delayed-scaling quantize %.4f ms (%.0f GB/s), current scaling %.4f ms" %
               (delayed["ms_delayed"], delayed["gbs_delayed"], delayed["ms_current"]), file=sys.stderr, flush=True)
+    mlp = None
+    if not args.no_block:
+        mlp = mlp_gelu_times(fp8, torch, synth, N, args.steps, args.warmup, args.reps, dev)
+        print("MLP block with GELU: fused %.4f ms, unfused %.4f ms; GELU quantize fused %.4f ms, unfused %.4f ms" %
+              (mlp["block"]["ms_fused"], mlp["block"]["ms_unfused"], mlp["tensor"]["gelu_fused"]["ms"],
+               mlp["tensor"]["gelu_unfused"]["ms"]), file=sys.stderr, flush=True)
     pages_tflops = sum(6 * 131072 * K * M for K, M in shapes) / (sum(PAGES_MS[s] for s in shapes) / 1e3) / 1e12
 
     out = {
@@ -599,6 +684,7 @@ def main():
         "amax_handoff": chain,
         "bf16_comparator": bf16,
         "delayed_scaling_quantize": delayed,
+        "mlp_gelu": mlp,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens)
