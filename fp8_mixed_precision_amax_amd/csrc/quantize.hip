@@ -7,7 +7,8 @@
 // (opening post): blockwise amax, no amax history.
 //
 // Kernels
-//   amax_partial_kernel   tensorwise amax, pass 1: grid-stride 16-byte loads,
+//   amax_partial_kernel<STREAM>
+//                         tensorwise amax, pass 1: grid-stride 16-byte loads,
 //                         packed 16-bit max on bf16 magnitude bits, wave and
 //                         workgroup reduction, one partial max per workgroup.
 //   cast_kernel<FMT,MODE> one wave per 128x128 tile, no LDS: lane (rb, cb)
@@ -46,13 +47,10 @@ namespace fp8k {
 
 constexpr int kAmaxThreads = 256;
 
-// One sweep of the tensor from front to back (grid-stride, one 16-byte load
-// per thread per step), so the cast that follows can start on the most
-// recently read data while it is still in the memory-side cache.  Partial
-// maxima are bf16 magnitude bits (16 bits); workgroup 0 zero-fills the
-// unused tail of the kMaxAmaxPartials slots so readers may scan all of them.
-// The workgroup's maximum of the threads' packed magnitude maxima m goes to
-// partial[blockIdx.x]; workgroup 0 zero-fills the unused slots.
+// Partial maxima are bf16 magnitude bits (16 bits): the workgroup's maximum
+// of the threads' packed magnitude maxima m goes to partial[blockIdx.x], and
+// workgroup 0 zero-fills the unused tail of the kMaxAmaxPartials slots so
+// readers may scan all of them.
 __device__ __forceinline__ void amax_store_partial(uint32_t m, uint16_t* __restrict__ partial) {
     m = wave_max_u32(hmax_u16(m));
     __shared__ uint32_t red[kAmaxThreads / 64];
@@ -71,11 +69,29 @@ __device__ __forceinline__ uint32_t mag8_max(uint32_t m, uint4 v) {
     return pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v.x), mag2(v.y)), pkmax_u16(mag2(v.z), mag2(v.w))));
 }
 
+// One sweep of the tensor from front to back (grid-stride).  A tensor that
+// fits the memory-side cache is read with ordinary loads, one 16-byte load
+// per thread per step, so the cast that follows (last tile first) finds the
+// most recently read data still cached.  A larger one cannot stay cached
+// (the cast gains nothing from the cache: measured) and is streamed with
+// four non-temporal loads in flight per thread: with one, the grid keeps
+// about 8 MiB of reads outstanding, half of what HBM's latency needs.
+template <bool STREAM>
 __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
                                                                     uint16_t* __restrict__ partial) {
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < n16; i += stride) m = mag8_max(m, x[i]);
+    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    if constexpr (STREAM) {
+        for (; i + 3 * stride < n16; i += 4 * stride) {
+            uint4 v[4];
+#pragma unroll
+            for (int k = 0; k < 4; k++) v[k] = ld_nt16(x + i + k * stride);
+#pragma unroll
+            for (int k = 0; k < 4; k++) m = mag8_max(m, v[k]);
+        }
+    }
+    for (; i < n16; i += stride) m = mag8_max(m, x[i]);
     amax_store_partial(m, partial);
 }
 
@@ -84,8 +100,16 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4*
 template <int ACT> constexpr uint32_t act_table_bytes() { return ACT == 2 ? kActEntries * 4 : kActEntries * 2; }
 
 // amax of GELU(x) (ACT 1) or of dGELU(x, x2) (ACT 2): the transform is
-// applied as in the cast, so both passes see the same bf16 values.
-template <int ACT>
+// applied as in the cast, so both passes see the same bf16 values.  Four
+// loads in flight per thread; non-temporal ones (STREAM) for inputs larger
+// than the memory-side cache, as in amax_partial_kernel.
+template <int ACT, bool STREAM>
+__device__ __forceinline__ uint4 amax_ld(const uint4* p) {
+    if constexpr (STREAM) return ld_nt16(p);
+    else return *p;
+}
+
+template <int ACT, bool STREAM>
 __global__ __launch_bounds__(kAmaxThreads) void act_amax_kernel(const uint4* __restrict__ x,
                                                                 const uint4* __restrict__ x2, int64_t n16,
                                                                 uint16_t* __restrict__ partial, const void* gtab) {
@@ -99,8 +123,8 @@ __global__ __launch_bounds__(kAmaxThreads) void act_amax_kernel(const uint4* __r
         uint4 v[4], u[4];
 #pragma unroll
         for (int k = 0; k < 4; k++) {
-            v[k] = ld_nt16(x + i + k * stride);
-            if constexpr (ACT == 2) u[k] = ld_nt16(x2 + i + k * stride);
+            v[k] = amax_ld<ACT, STREAM>(x + i + k * stride);
+            if constexpr (ACT == 2) u[k] = amax_ld<ACT, STREAM>(x2 + i + k * stride);
         }
 #pragma unroll
         for (int k = 0; k < 4; k++)
@@ -108,9 +132,9 @@ __global__ __launch_bounds__(kAmaxThreads) void act_amax_kernel(const uint4* __r
                                      : dgelu8(v[k], u[k], reinterpret_cast<const float*>(tab)));
     }
     for (; i < n16; i += stride) {
-        const uint4 v = ld_nt16(x + i);
+        const uint4 v = x[i];
         m = mag8_max(m, ACT == 1 ? gelu8(v, reinterpret_cast<const uint16_t*>(tab))
-                                 : dgelu8(v, ld_nt16(x2 + i), reinterpret_cast<const float*>(tab)));
+                                 : dgelu8(v, x2[i], reinterpret_cast<const float*>(tab)));
     }
     amax_store_partial(m, partial);
 }
@@ -504,13 +528,18 @@ hipError_t launch_act_quantize(const QuantizeLaunch& q, CastArgs& a, hipStream_t
         const int64_t n16 = q.rows * q.cols / 8;
         int64_t g = (n16 + (int64_t)kAmaxThreads * 16 - 1) / ((int64_t)kAmaxThreads * 16);
         g = g < 1 ? 1 : (g > 512 ? 512 : g);
-        if (q.act == 1)
-            hipLaunchKernelGGL(act_amax_kernel<1>, dim3((unsigned)g), dim3(kAmaxThreads), 0, stream,
-                               static_cast<const uint4*>(q.x), nullptr, n16, q.partial, a.act_tab);
-        else
-            hipLaunchKernelGGL(act_amax_kernel<2>, dim3((unsigned)g), dim3(kAmaxThreads), 0, stream,
-                               static_cast<const uint4*>(q.x), static_cast<const uint4*>(q.x2), n16, q.partial,
-                               a.act_tab);
+        const bool big = q.rows * q.cols * 2 * (q.act == 2 ? 2 : 1) > (int64_t(256) << 20);
+        const uint4* x = static_cast<const uint4*>(q.x);
+        const uint4* x2 = static_cast<const uint4*>(q.x2);
+#define FP8K_AMAX(A, S) \
+    hipLaunchKernelGGL((act_amax_kernel<A, S>), dim3((unsigned)g), dim3(kAmaxThreads), 0, stream, x, x2, n16, \
+                       q.partial, a.act_tab)
+        if (q.act == 1) {
+            if (big) FP8K_AMAX(1, true); else FP8K_AMAX(1, false);
+        } else {
+            if (big) FP8K_AMAX(2, true); else FP8K_AMAX(2, false);
+        }
+#undef FP8K_AMAX
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -555,8 +584,13 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     if (q.act) return launch_act_quantize(q, a, stream);
     if (q.scaling == 0 && !q.partial_given) {
         const int g = amax_partial_count(q.rows * q.cols);
-        hipLaunchKernelGGL(amax_partial_kernel, dim3(g), dim3(kAmaxThreads), 0, stream,
-                           static_cast<const uint4*>(q.x), q.rows * q.cols / 8, q.partial);
+        // above 256 MiB of bf16 the tensor outgrows the memory-side cache
+        if (q.rows * q.cols * 2 > (int64_t(256) << 20))
+            hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(g), dim3(kAmaxThreads), 0, stream,
+                               static_cast<const uint4*>(q.x), q.rows * q.cols / 8, q.partial);
+        else
+            hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(g), dim3(kAmaxThreads), 0, stream,
+                               static_cast<const uint4*>(q.x), q.rows * q.cols / 8, q.partial);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
