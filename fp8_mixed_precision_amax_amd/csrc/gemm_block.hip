@@ -184,7 +184,7 @@ __device__ __forceinline__ void promote_rows(v16f& acc, const v16f& p, float sa,
         acc[4 * q + 3] = __builtin_fmaf(p[4 * q + 3], sa * sb[q].w, acc[4 * q + 3]);
     }
 }
-template <int FA, int FB>
+template <int FA, int FB, bool NT>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
     // separate objects: the epilogue's LDS traffic never aliases the stages
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
                 }
                 u32x4 r;
                 asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(raddr) : "memory");
-                *reinterpret_cast<u32x4*>(ob + (int64_t)(mi * 32 + pg * 8) * g.J * 2) = r;
+                st_out16<NT>(ob + (int64_t)(mi * 32 + pg * 8) * g.J * 2, r);
             }
         return 8;
     };
@@ -479,12 +479,14 @@ hipError_t launch_gemm_block(const GemmLaunch& l, int splits, hipStream_t stream
     g.gi = 8;
     int grid = cu_count();
     if (grid > g.items) grid = g.items;
-#define FP8K_LAUNCH(FA, FB) \
-    hipLaunchKernelGGL((gemm_block_kernel<FA, FB>), dim3(grid), dim3(NW * 64), 0, stream, g)
-    if (l.fa == 0 && l.fb == 0) FP8K_LAUNCH(0, 0);
-    else if (l.fa == 1 && l.fb == 0) FP8K_LAUNCH(1, 0);
-    else if (l.fa == 0 && l.fb == 1) FP8K_LAUNCH(0, 1);
-    else FP8K_LAUNCH(1, 1);
+    const bool nt = l.K <= kNtMaxContraction;
+#define FP8K_LAUNCH(FA, FB)                                                                                    \
+    if (nt) hipLaunchKernelGGL((gemm_block_kernel<FA, FB, true>), dim3(grid), dim3(NW * 64), 0, stream, g);  \
+    else hipLaunchKernelGGL((gemm_block_kernel<FA, FB, false>), dim3(grid), dim3(NW * 64), 0, stream, g)
+    if (l.fa == 0 && l.fb == 0) { FP8K_LAUNCH(0, 0); }
+    else if (l.fa == 1 && l.fb == 0) { FP8K_LAUNCH(1, 0); }
+    else if (l.fa == 0 && l.fb == 1) { FP8K_LAUNCH(0, 1); }
+    else { FP8K_LAUNCH(1, 1); }
 #undef FP8K_LAUNCH
     return hipGetLastError();
 }

@@ -151,7 +151,7 @@ __device__ __forceinline__ void read_a(v8i (&fa)[2], uint32_t a0, uint32_t a1) {
     fa[1] = __builtin_bit_cast(v8i, __builtin_shufflevector(x2, x3, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool NT>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_block_wide_kernel(Args g) {
     // separate objects: the epilogue's LDS traffic never aliases the stages
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
@@ -323,8 +323,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_wide_kernel(Args g) {
                              : "v"(ra0), "v"(ra1)
                              : "memory");
                 uint8_t* o = ob + (int64_t)(mi * 32 + pg * 16) * g.J * 2;
-                *reinterpret_cast<u32x4*>(o) = r0;
-                *reinterpret_cast<u32x4*>(o + (int64_t)8 * g.J * 2) = r1;
+                st_out16<NT>(o, r0);
+                st_out16<NT>(o + (int64_t)8 * g.J * 2, r1);
             }
         return 16;
     };
@@ -421,12 +421,14 @@ hipError_t launch_gemm_block_wide(const GemmLaunch& l, int splits, hipStream_t s
     g.gi = g.tiles_j >= 16 ? 8 : 2;
     int grid = cu_count();
     if (grid > g.items) grid = g.items;
-#define FP8K_LAUNCH(FA, FB) \
-    hipLaunchKernelGGL((gemm_block_wide_kernel<FA, FB>), dim3(grid), dim3(NW * 64), 0, stream, g)
-    if (l.fa == 0 && l.fb == 0) FP8K_LAUNCH(0, 0);
-    else if (l.fa == 1 && l.fb == 0) FP8K_LAUNCH(1, 0);
-    else if (l.fa == 0 && l.fb == 1) FP8K_LAUNCH(0, 1);
-    else FP8K_LAUNCH(1, 1);
+    const bool nt = l.K <= kNtMaxContraction;
+#define FP8K_LAUNCH(FA, FB)                                                                                         \
+    if (nt) hipLaunchKernelGGL((gemm_block_wide_kernel<FA, FB, true>), dim3(grid), dim3(NW * 64), 0, stream, g);  \
+    else hipLaunchKernelGGL((gemm_block_wide_kernel<FA, FB, false>), dim3(grid), dim3(NW * 64), 0, stream, g)
+    if (l.fa == 0 && l.fb == 0) { FP8K_LAUNCH(0, 0); }
+    else if (l.fa == 1 && l.fb == 0) { FP8K_LAUNCH(1, 0); }
+    else if (l.fa == 0 && l.fb == 1) { FP8K_LAUNCH(0, 1); }
+    else { FP8K_LAUNCH(1, 1); }
 #undef FP8K_LAUNCH
     return hipGetLastError();
 }

@@ -11,6 +11,21 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes of the bf16 output.  NT: a non-temporal (streaming) store.  The
+// bf16 output of a short contraction is large next to its operands and
+// leaves the GPU anyway; streamed, its stores retire faster, and the next
+// tile's operand loads, issued after them and waited for in order with them
+// (one vmcnt for loads and stores), stall less: 131072 x 2048 x 512
+// 203 -> 144 us, 131072 x 512 x 2048 127 -> 115 us; on 8192^3, where the
+// output is small next to the contraction, 375 -> 399 us, so only
+// contractions up to 2048 use them.
+template <bool NT>
+__device__ __forceinline__ void st_out16(void* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+}
+constexpr int64_t kNtMaxContraction = 2048;
+
 // One v_mfma_f32_32x32x64_f8f6f4 (scale operands 0: the unscaled form).
 // Matrix-core operand 0 = B fragment (rows j), operand 1 = A fragment (rows i),
 // so each lane's accumulators hold one output row i and runs of 4 columns j.

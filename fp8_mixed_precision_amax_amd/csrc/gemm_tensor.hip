@@ -114,7 +114,7 @@ __device__ __forceinline__ void wait_vm_n(int n) {
     else wait_vm<0>();
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool NT>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     // separate objects: the epilogue's LDS traffic never aliases the stages
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
@@ -280,10 +280,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
             asm volatile("ds_read_b128 %0, %1" : "=v"(r3) : "v"(ra3) : "memory");
             asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r0), "+v"(r1), "+v"(r2), "+v"(r3));
             uint8_t* ob = out_base + (int64_t)mi * 32 * g.J * 2;
-            *reinterpret_cast<u32x4*>(ob + goff) = r0;
-            *reinterpret_cast<u32x4*>(ob + (int64_t)8 * g.J * 2 + goff) = r1;
-            *reinterpret_cast<u32x4*>(ob + (int64_t)16 * g.J * 2 + goff) = r2;
-            *reinterpret_cast<u32x4*>(ob + (int64_t)24 * g.J * 2 + goff) = r3;
+            st_out16<NT>(ob + goff, r0);
+            st_out16<NT>(ob + (int64_t)8 * g.J * 2 + goff, r1);
+            st_out16<NT>(ob + (int64_t)16 * g.J * 2 + goff, r2);
+            st_out16<NT>(ob + (int64_t)24 * g.J * 2 + goff, r3);
         }
         return 4 * 4;
     };
@@ -431,12 +431,14 @@ hipError_t launch_gemm_tensor(const GemmLaunch& l, int splits, hipStream_t strea
     g.gi = g.tiles_j >= 16 ? 8 : 2;
     int grid = cu_count();
     if (grid > g.items) grid = g.items;
-#define FP8K_LAUNCH(FA, FB) \
-    hipLaunchKernelGGL((gemm_tensor_kernel<FA, FB>), dim3(grid), dim3(NW * 64), 0, stream, g)
-    if (l.fa == 0 && l.fb == 0) FP8K_LAUNCH(0, 0);
-    else if (l.fa == 1 && l.fb == 0) FP8K_LAUNCH(1, 0);
-    else if (l.fa == 0 && l.fb == 1) FP8K_LAUNCH(0, 1);
-    else FP8K_LAUNCH(1, 1);
+    const bool nt = l.K <= kNtMaxContraction;
+#define FP8K_LAUNCH(FA, FB)                                                                                     \
+    if (nt) hipLaunchKernelGGL((gemm_tensor_kernel<FA, FB, true>), dim3(grid), dim3(NW * 64), 0, stream, g);  \
+    else hipLaunchKernelGGL((gemm_tensor_kernel<FA, FB, false>), dim3(grid), dim3(NW * 64), 0, stream, g)
+    if (l.fa == 0 && l.fb == 0) { FP8K_LAUNCH(0, 0); }
+    else if (l.fa == 1 && l.fb == 0) { FP8K_LAUNCH(1, 0); }
+    else if (l.fa == 0 && l.fb == 1) { FP8K_LAUNCH(0, 1); }
+    else { FP8K_LAUNCH(1, 1); }
 #undef FP8K_LAUNCH
     return hipGetLastError();
 }
