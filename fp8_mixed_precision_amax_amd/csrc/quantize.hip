@@ -21,8 +21,11 @@
 //                         groups make every transposed store instruction
 //                         write whole 64-byte spans (4 lanes x 16 bytes),
 //                         issued as ordinary write-back stores so the L2
-//                         merges them; the row layout goes out with
-//                         non-temporal 8-byte stores (16 lanes = 128 bytes).
+//                         merges them; the row layout goes out with 8-byte
+//                         stores (16 lanes = 128 bytes), ordinary ones when
+//                         it fits the memory-side cache (the GEMM that
+//                         follows reads it back from there), non-temporal
+//                         otherwise.
 //     MODE 0 tensorwise: the scale is rebuilt in each wave from the amax
 //            partials of pass 1 (so the cast needs no separate launch).
 //     MODE 1 1x128 blocks: row blocks reduce over the 16 lanes of a DPP row;
@@ -155,7 +158,18 @@ struct CastArgs {
     uint16_t* tile_amax;      // delayed only: amax of each 128x128 tile (bf16 magnitude bits)
     const uint16_t* x2;       // dGELU only: GELU's input [R, C]; x is the gradient of its output
     const void* act_tab;      // GELU / GELU' table (global memory), act_cast_kernel only
+    int row_cached;           // row layout with ordinary (cached) stores instead of non-temporal
 };
+
+// 8 bytes of the row layout.  The GEMM that follows a quantize reads its row
+// layout at once: up to 128 MiB it is written with ordinary stores and read
+// back from the memory-side cache (131072 x 2048 x 512 GEMM after the
+// quantize of its 64 MiB operand: 186 -> 155 us), larger ones would evict
+// more than they keep (the two 256 MiB cases slowed by 6-9 us) and stream.
+__device__ __forceinline__ void st_row8(const CastArgs& a, uint8_t* p, uint2 w) {
+    if (a.row_cached) *reinterpret_cast<uint2*>(p) = w;
+    else st_nt8(p, w);
+}
 
 // One 128x128 tile, by one wave.  slot < number of tiles.  ACT 1 / 2 encode
 // GELU(x) / dGELU(x, x2) instead of x (tab: the table in LDS).
@@ -322,7 +336,7 @@ __device__ __forceinline__ void cast_tile(const CastArgs& a, int64_t slot, const
         }
         if (a.q_row) {
 #pragma unroll
-            for (int i = 0; i < 32; i++) st_nt8(a.q_row + FP8K_ROW(i) * a.C + col0, code[i]);
+            for (int i = 0; i < 32; i++) st_row8(a, a.q_row + FP8K_ROW(i) * a.C + col0, code[i]);
         }
         if (a.q_col) {
             uint32_t t[8][8];   // t[column j][row group h]
@@ -385,7 +399,7 @@ __device__ __forceinline__ void cast_tile(const CastArgs& a, int64_t slot, const
                     const int i = 2 * p + h;
                     uint2 c = enc8<FMT>(v[i], h ? sp1 : sp0);
                     if (nan_rows) c = patch_nan8(v[i], c);
-                    st_nt8(a.q_row + FP8K_ROW(i) * a.C + col0, c);
+                    st_row8(a, a.q_row + FP8K_ROW(i) * a.C + col0, c);
                 }
             }
         }
@@ -581,6 +595,7 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     a.tile_amax = q.partial;
     a.x2 = static_cast<const uint16_t*>(q.x2);
     a.act_tab = nullptr;
+    a.row_cached = q.rows * q.cols <= (int64_t(128) << 20);
     if (q.act) return launch_act_quantize(q, a, stream);
     if (q.scaling == 0 && !q.partial_given) {
         const int g = amax_partial_count(q.rows * q.cols);
