@@ -325,6 +325,119 @@ def make_layers(fp8, torch, synth, N, recipe, dev):
     return layers
 
 
+def workload_layers(fp8, torch, synth, name, dev):
+    """One linear of a named synthetic workload (its own distributions and
+    recipe), in the form stage_times and time_steps take."""
+    wl = synth.workload_on_device(name, seed=0, device=dev)
+    N, K, M = wl["N"], wl["K"], wl["M"]
+    R = fp8.RECIPE_BLOCK if wl["scaling"] == "block" else fp8.RECIPE_TENSOR
+    return [{"N": N, "K": K, "M": M, "x": wl["x"], "w": wl["w"], "dy": wl["dy"],
+             "lin": fp8.Fp8Linear(N, K, M, R, device=dev),
+             "y": torch.empty((N, M), dtype=torch.bfloat16, device=dev),
+             "dx": torch.empty((N, K), dtype=torch.bfloat16, device=dev),
+             "dw": torch.empty((M, K), dtype=torch.bfloat16, device=dev)}], wl["scaling"]
+
+
+MFMA_PEAK_TFLOPS = 5000.0   # dense FP8 matrix-core peak of the MI355X (vendor figure)
+
+
+def config_times(fp8, torch, synth, steps, warmup, reps, dev):
+    """The other linear workloads: the block-scaled 512->8192 at N=131072
+    (1% outliers), the square 8192x8192 weight at N=16384 and 512->8192 at
+    N=262144 under both recipes.  For each: forward + backward time (every
+    quantization included) and each GEMM's rate against the dense FP8 peak."""
+    names = ["linear_512x8192_n131072_block", "linear_8192x8192_n16384", "linear_8192x8192_n16384_block",
+             "linear_512x8192_n262144", "linear_512x8192_n262144_block"]
+    out = {}
+    for name in names:
+        layers, recipe = workload_layers(fp8, torch, synth, name, dev)
+        L = layers[0]
+        ms = time_steps(torch, layers, steps, warmup)
+        st, _ = stage_times(fp8, torch, layers, reps, recipe)
+        flops = 6 * L["N"] * L["K"] * L["M"]
+        gemms = {}
+        for s in st:
+            if "flops" in s:
+                gemms[s["stage"].split("_")[1]] = {"ms": round(s["ms"], 4), "tflops": round(s["tflops"], 1),
+                                                   "mfma_frac": round(s["tflops"] / MFMA_PEAK_TFLOPS, 3)}
+        quant = {s["stage"].split("_")[1]: {"ms": round(s["ms"], 4), "gbs": round(s["gbs"], 1)}
+                 for s in st if "flops" not in s}
+        out[name] = {"recipe": recipe, "N": L["N"], "K": L["K"], "M": L["M"], "ms_per_step": round(ms, 4),
+                     "value": round(flops / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s", "gemms": gemms,
+                     "quantize": quant}
+        print("%s: %.4f ms/step, %.1f TFLOP/s; GEMMs %s" % (name, ms, out[name]["value"],
+              ", ".join("%s %.0f" % (k, v["tflops"]) for k, v in gemms.items())), file=sys.stderr, flush=True)
+        del layers, L
+        torch.cuda.empty_cache()
+    return out
+
+
+def _gelu_ref(torch, a):
+    x = a.float()
+    return (0.5 * x * (1.0 + torch.erf(x * 0.7071067811865476))).to(torch.bfloat16)
+
+
+def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8, mbs=4):
+    """The MLP stack of the gradient-accumulation workload: `layers` blocks of
+    512 -> 2048 (GELU) -> 512, `mbs` microbatches of N tokens per cycle, the
+    GELU fused into the quantizers.  Timed over `cycles` cycles (one untimed
+    first) with the weight cache (W quantized on microbatch 1, reused on the
+    rest) and without it (W requantized every microbatch)."""
+    d, h = 512, 2048
+    R = fp8.RECIPE_BLOCK if recipe == "block" else fp8.RECIPE_TENSOR
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    weights = []
+    for _ in range(layers):
+        weights.append(synth.normal_bf16((h, d), 0.02, g, device=dev))
+        weights.append(synth.normal_bf16((d, h), 0.02, g, device=dev))
+    xs = [synth.normal_bf16((N, d), 1.0, g, device=dev) for _ in range(mbs)]
+    dys = [synth.normal_bf16((N, d), 1e-3, g, device=dev) for _ in range(mbs)]
+    shapes = [(d, h), (h, d)] * layers
+    res = {}
+    for cached in (True, False):
+        lins = [fp8.Fp8Linear(N, K, M, R, device=dev, cache=cached) for K, M in shapes]
+        pre = [torch.empty((N, h), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+        hid = [torch.empty((N, d), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
+        dws = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for K, M in shapes]
+        dg = torch.empty((N, h), dtype=torch.bfloat16, device=dev)
+        dh = [torch.empty((N, d), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+
+        def cycle():
+            for mb in range(mbs):
+                flag = (mb == 0) if cached else None
+                x = xs[mb]
+                for p in range(layers):
+                    lins[2 * p].forward(x, weights[2 * p], y=pre[p], is_first_microbatch=flag)
+                    lins[2 * p + 1].forward(pre[p], weights[2 * p + 1], y=hid[p], is_first_microbatch=flag,
+                                            gelu=True)
+                    x = hid[p]
+                g_in = dys[mb]
+                for p in reversed(range(layers)):
+                    lins[2 * p + 1].backward(g_in, dx=dg, dw=dws[2 * p + 1])
+                    out = dh[p & 1]
+                    lins[2 * p].backward(dg, dx=out, dw=dws[2 * p], gelu_input=pre[p])
+                    g_in = out
+        cycle()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(cycles):
+            cycle()
+        e1.record()
+        torch.cuda.synchronize()
+        res[cached] = e0.elapsed_time(e1) / cycles
+        del lins, pre, hid, dws, dg, dh
+        torch.cuda.empty_cache()
+    flops = mbs * sum(6 * N * K * M for K, M in shapes)
+    return {"workload": "%d x (512->2048, GELU, 2048->512), N=%d per microbatch, %d microbatches per cycle, %s"
+                        % (layers, N, mbs, "tensorwise" if recipe == "tensor" else "1x128 / 128x128 blocks"),
+            "ms_per_cycle_cached": round(res[True], 3), "ms_per_cycle_uncached": round(res[False], 3),
+            "value_cached": round(flops / (res[True] / 1e3) / 1e12, 2),
+            "value_uncached": round(flops / (res[False] / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+            "cache_speedup": round(res[False] / res[True], 4)}
+
+
 def time_steps(torch, layers, steps, warmup):
     """ms per step (events around `steps` steps after `warmup` untimed ones)."""
     def step():
@@ -664,6 +777,14 @@ def main():
         print("MLP block with GELU: fused %.4f ms, unfused %.4f ms; GELU quantize fused %.4f ms, unfused %.4f ms" %
               (mlp["block"]["ms_fused"], mlp["block"]["ms_unfused"], mlp["tensor"]["gelu_fused"]["ms"],
                mlp["tensor"]["gelu_unfused"]["ms"]), file=sys.stderr, flush=True)
+    configs = None
+    stack = None
+    if not args.no_block:
+        configs = config_times(fp8, torch, synth, args.steps, args.warmup, args.reps, dev)
+        stack = {r: mlp_stack_times(fp8, torch, synth, N, 2, dev, r) for r in ("tensor", "block")}
+        for r, v in stack.items():
+            print("MLP stack (%s): %.3f ms/cycle cached, %.3f uncached" %
+                  (r, v["ms_per_cycle_cached"], v["ms_per_cycle_uncached"]), file=sys.stderr, flush=True)
     pages_tflops = sum(6 * 131072 * K * M for K, M in shapes) / (sum(PAGES_MS[s] for s in shapes) / 1e3) / 1e12
 
     out = {
@@ -685,6 +806,8 @@ def main():
         "bf16_comparator": bf16,
         "delayed_scaling_quantize": delayed,
         "mlp_gelu": mlp,
+        "other_configs": configs,
+        "mlp_stack_weight_cache": stack,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens)

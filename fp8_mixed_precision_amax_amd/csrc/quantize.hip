@@ -522,9 +522,14 @@ __global__ __launch_bounds__(256) void history_update_kernel(const uint16_t* __r
 }
 
 int amax_partial_count(int64_t numel) {
-    // about eight workgroups per CU, one 16-byte load per thread per sweep step
+    // about eight workgroups per CU, one 16-byte load per thread per sweep
+    // step; a small tensor (a weight) gets up to 512 workgroups of one load
+    // per thread instead of a few workgroups of sixteen dependent steps
     const int64_t n16 = numel / 8;
     int64_t g = (n16 + (int64_t)kAmaxThreads * 16 - 1) / ((int64_t)kAmaxThreads * 16);
+    int64_t g1 = (n16 + kAmaxThreads - 1) / kAmaxThreads;
+    if (g1 > 512) g1 = 512;
+    if (g < g1) g = g1;
     if (g < 1) g = 1;
     if (g > kMaxAmaxPartials) g = kMaxAmaxPartials;
     return (int)g;
