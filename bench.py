@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-stage breakdown")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings (HBM probes, sustained GEMM clock)")
     ap.add_argument("--no-block", action="store_true", help="skip the block-scaling, stacked-linear (amax hand-off), BF16 comparator and delayed-scaling runs")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after the steps, negate a 512 MiB fp16 tensor (counter calibration)")
@@ -105,7 +106,7 @@ def source_digest():
     files = sorted(glob.glob(os.path.join(ROOT, "fp8_mixed_precision_amax_amd", "csrc", "*")) +
                    glob.glob(os.path.join(ROOT, "include", "*.h")))
     for f in files:
-        if f.endswith((".hip", ".hpp", ".cpp", ".h")):
+        if f.endswith((".hip", ".hpp", ".cpp", ".h")) and os.path.basename(f) != "ceilings.hip":
             h.update(os.path.basename(f).encode())
             with open(f, "rb") as fh:
                 h.update(fh.read())
@@ -436,6 +437,137 @@ def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8
             "value_cached": round(flops / (res[True] / 1e3) / 1e12, 2),
             "value_uncached": round(flops / (res[False] / 1e3) / 1e12, 2), "unit": "TFLOP/s",
             "cache_speedup": round(res[False] / res[True], 4)}
+
+
+def _amd_smi_sample():
+    """GFX clocks (MHz, one per XCD) and socket power (W) from `amd-smi
+    metric`, or None where the tool is missing or prints no such fields."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "-p"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    txt = r.stdout
+    clocks = []
+    for blk in re.split(r"\n\s*GFX_\d+:", txt)[1:]:
+        m = re.search(r"^\s*CLK:\s*(\d+)\s*MHz", blk, re.M)
+        if m:
+            clocks.append(int(m.group(1)))
+    pw = re.search(r"SOCKET_POWER:\s*(\d+)\s*W", txt)
+    if not clocks:
+        return None
+    return {"gfx_mhz": clocks, "socket_power_w": int(pw.group(1)) if pw else None}
+
+
+def ceilings(fp8, torch, synth, dev):
+    """What this GPU reaches with plain kernels (libfp8ceilings.so): HBM
+    read, write and copy bandwidth on a 2 GiB buffer (eight times the
+    memory-side cache; best launch of a few), the rate of back-to-back FP8
+    matrix-core instructions with the shader clock they ran at, and the GFX
+    clock and socket power while 8192 x 8192 x 16384 FP8 GEMMs of the library
+    run back to back for about two seconds."""
+    import ctypes
+    import threading
+    path = os.path.join(ROOT, "fp8_mixed_precision_amax_amd", "libfp8ceilings.so")
+    if not os.path.exists(path):
+        return None
+    cl = ctypes.CDLL(path)
+    cl.fp8c_hbm_read.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                 ctypes.c_void_p]
+    cl.fp8c_hbm_write.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    cl.fp8c_hbm_copy.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    cl.fp8c_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 2 << 30
+    n16 = nbytes // 16
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    y = torch.empty_like(x)
+    o = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def best(fn, moved):
+        rates = []
+        for grid in (1024, 2048, 4096, 8192):
+            if fn(grid) != 0:
+                raise RuntimeError("ceiling probe launch failed")
+            ms = _ms(torch, lambda: fn(grid), 10)
+            rates.append(moved / ms / 1e6)
+        return round(max(rates), 1)
+
+    res = {"hbm_buffer_bytes": nbytes}
+    res["hbm_read_gbs"] = max(best(lambda g, v=v: cl.fp8c_hbm_read(v, g, x.data_ptr(), n16, o.data_ptr(), st), nbytes)
+                              for v in (0, 1))
+    res["hbm_write_gbs"] = max(best(lambda g, v=v: cl.fp8c_hbm_write(v, g, y.data_ptr(), n16, st), nbytes)
+                               for v in (0, 1))
+    res["hbm_copy_gbs"] = best(lambda g: cl.fp8c_hbm_copy(g, x.data_ptr(), y.data_ptr(), n16, st), 2 * nbytes)
+    res["hbm_copy_gbs_torch"] = round(2 * nbytes / _ms(torch, lambda: y.copy_(x), 10) / 1e6, 1)
+    del x, y
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid, block, iters = 2 * cus, 512, 20000
+    out = torch.empty(grid * block, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2 * grid, dtype=torch.int64, device=dev)
+    run = lambda: cl.fp8c_mfma(grid, block, iters, out.data_ptr(), clk.data_ptr(), st)
+    if run() != 0:
+        raise RuntimeError("ceiling probe launch failed")
+    ms = _ms(torch, run, 3)
+    c = clk.view(grid, 2).double().cpu()
+    res["mfma_only_tflops"] = round(grid * (block // 64) * iters * 4 * (2 * 32 * 32 * 64) / ms / 1e9, 1)
+    res["mfma_only_shader_ghz"] = round(float((c[:, 0] / (c[:, 1] / 100e6)).mean()) / 1e9, 3)
+
+    # sustained GEMM: clock and power as the power limit sees them
+    I = J = 8192
+    K = 16384
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    qa = fp8.quantize(synth.normal_bf16((I, K), 1.0, g, device=dev), fp8.E4M3, layouts=fp8.LAYOUT_ROW)
+    qb = fp8.quantize(synth.normal_bf16((J, K), 1.0, g, device=dev), fp8.E4M3, layouts=fp8.LAYOUT_ROW)
+    cout = torch.empty((I, J), dtype=torch.bfloat16, device=dev)
+    sa, sb = fp8.gemm_scale(qa.scale_inv), fp8.gemm_scale(qb.scale_inv)
+    gemm = lambda: fp8.gemm(qa.q_row, fp8.E4M3, sa, qb.q_row, fp8.E4M3, sb, out=cout)
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        time.sleep(0.5)
+        while not stop.is_set():
+            s = _amd_smi_sample()
+            if s is None:
+                return
+            samples.append(s)
+            time.sleep(0.2)
+
+    for _ in range(3):
+        gemm()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler)
+    th.start()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < 2.5:
+        for _ in range(16):
+            gemm()
+        n += 16
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    ms = e0.elapsed_time(e1) / n
+    gt = {"workload": "%dx%dx%d tensorwise FP8 GEMM, back to back for %.1f s" % (I, J, K, time.perf_counter() - t0),
+          "tflops": round(2 * I * J * K / ms / 1e9, 1), "samples": len(samples)}
+    if samples:
+        mhz = [sum(s["gfx_mhz"]) / len(s["gfx_mhz"]) for s in samples]
+        gt["gfx_mhz_mean"] = round(sum(mhz) / len(mhz))
+        pw = [s["socket_power_w"] for s in samples if s["socket_power_w"] is not None]
+        gt["socket_power_w_mean"] = round(sum(pw) / len(pw)) if pw else None
+        # the dense FP8 peak scales with the clock: 256 CUs x 8192 FLOP per clock
+        gt["mfma_peak_at_that_clock_tflops"] = round(256 * 8192 * gt["gfx_mhz_mean"] * 1e6 / 1e12, 1)
+        gt["frac_of_clock_peak"] = round(gt["tflops"] / gt["mfma_peak_at_that_clock_tflops"], 3)
+    res["sustained_gemm"] = gt
+    return res
 
 
 def time_steps(torch, layers, steps, warmup):
@@ -785,6 +917,14 @@ def main():
         for r, v in stack.items():
             print("MLP stack (%s): %.3f ms/cycle cached, %.3f uncached" %
                   (r, v["ms_per_cycle_cached"], v["ms_per_cycle_uncached"]), file=sys.stderr, flush=True)
+    ceil = None
+    if not args.no_block and not args.no_ceilings:
+        ceil = ceilings(fp8, torch, synth, dev)
+        if ceil:
+            print("ceilings: HBM read %.0f, write %.0f, copy %.0f GB/s; MFMA-only %.0f TFLOP/s at %.2f GHz; "
+                  "sustained GEMM %s" % (ceil["hbm_read_gbs"], ceil["hbm_write_gbs"], ceil["hbm_copy_gbs"],
+                                         ceil["mfma_only_tflops"], ceil["mfma_only_shader_ghz"],
+                                         ceil["sustained_gemm"]), file=sys.stderr, flush=True)
     pages_tflops = sum(6 * 131072 * K * M for K, M in shapes) / (sum(PAGES_MS[s] for s in shapes) / 1e3) / 1e12
 
     out = {
@@ -808,6 +948,7 @@ def main():
         "mlp_gelu": mlp,
         "other_configs": configs,
         "mlp_stack_weight_cache": stack,
+        "ceilings": ceil,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens)
