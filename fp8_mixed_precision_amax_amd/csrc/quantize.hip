@@ -467,7 +467,7 @@ __device__ __forceinline__ void cast_tile(const CastArgs& a, int64_t slot, const
 template <int FMT, int MODE>
 __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     const int64_t ntiles = (a.R >> 7) * (a.C >> 7);
-    const int64_t slot = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t slot = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     if (slot >= ntiles) return;
     cast_tile<FMT, MODE, 0>(a, slot, nullptr);
 }
@@ -614,9 +614,13 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // four waves (tiles) per workgroup; a small tensor (a weight: 64 tiles
+    // for 2048 x 512) takes one wave per workgroup, so its tiles spread over
+    // as many CUs as there are tiles
     const int64_t ntiles = (q.rows / 128) * (q.cols / 128);
-    const dim3 grid((unsigned)((ntiles + 3) / 4));
-#define FP8K_CAST(F, M) hipLaunchKernelGGL((cast_kernel<F, M>), grid, dim3(256), 0, stream, a)
+    const int wpg = ntiles < 1024 ? 1 : 4;
+    const dim3 grid((unsigned)((ntiles + wpg - 1) / wpg));
+#define FP8K_CAST(F, M) hipLaunchKernelGGL((cast_kernel<F, M>), grid, dim3(64 * wpg), 0, stream, a)
     if (q.format == 0) {
         if (q.scaling == 0) FP8K_CAST(0, 0);
         else if (q.scaling == 1) FP8K_CAST(0, 1);
