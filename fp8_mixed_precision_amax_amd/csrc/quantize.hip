@@ -49,6 +49,7 @@
 namespace fp8k {
 
 constexpr int kAmaxThreads = 256;
+constexpr int kAmaxStreamThreads = 1024;   // the streamed sweep: 4x the threads, same partial count
 
 // Partial maxima are bf16 magnitude bits (16 bits): the workgroup's maximum
 // of the threads' packed magnitude maxima m goes to partial[blockIdx.x], and
@@ -56,16 +57,16 @@ constexpr int kAmaxThreads = 256;
 // readers may scan all of them.
 __device__ __forceinline__ void amax_store_partial(uint32_t m, uint16_t* __restrict__ partial) {
     m = wave_max_u32(hmax_u16(m));
-    __shared__ uint32_t red[kAmaxThreads / 64];
+    __shared__ uint32_t red[kAmaxStreamThreads / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t r = red[0];
-        for (int w = 1; w < kAmaxThreads / 64; w++) r = r > red[w] ? r : red[w];
+        for (int w = 1; w < (int)(blockDim.x >> 6); w++) r = r > red[w] ? r : red[w];
         partial[blockIdx.x] = (uint16_t)r;
     }
     if (blockIdx.x == 0)
-        for (int p = (int)gridDim.x + threadIdx.x; p < kMaxAmaxPartials; p += kAmaxThreads) partial[p] = 0;
+        for (int p = (int)gridDim.x + threadIdx.x; p < kMaxAmaxPartials; p += (int)blockDim.x) partial[p] = 0;
 }
 
 __device__ __forceinline__ uint32_t mag8_max(uint32_t m, uint4 v) {
@@ -80,11 +81,11 @@ __device__ __forceinline__ uint32_t mag8_max(uint32_t m, uint4 v) {
 // four non-temporal loads in flight per thread: with one, the grid keeps
 // about 8 MiB of reads outstanding, half of what HBM's latency needs.
 template <bool STREAM>
-__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
-                                                                    uint16_t* __restrict__ partial) {
+__global__ __launch_bounds__(kAmaxStreamThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                                          uint16_t* __restrict__ partial) {
     uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if constexpr (STREAM) {
         for (; i + 3 * stride < n16; i += 4 * stride) {
             uint4 v[4];
@@ -606,7 +607,7 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
         const int g = amax_partial_count(q.rows * q.cols);
         // above 256 MiB of bf16 the tensor outgrows the memory-side cache
         if (q.rows * q.cols * 2 > (int64_t(256) << 20))
-            hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(g), dim3(kAmaxThreads), 0, stream,
+            hipLaunchKernelGGL(amax_partial_kernel<true>, dim3(g), dim3(kAmaxStreamThreads), 0, stream,
                                static_cast<const uint4*>(q.x), q.rows * q.cols / 8, q.partial);
         else
             hipLaunchKernelGGL(amax_partial_kernel<false>, dim3(g), dim3(kAmaxThreads), 0, stream,
