@@ -224,3 +224,19 @@ def test_gelu_argument_errors(L):
     assert fwd(N=200) == SHAPE
     assert fwd(wq=False) == NULL                           # None (-1) needs w_q
     assert bwd(y_pre=None) == NULL and bwd(y_pre=U) == ALIGN
+
+
+def test_ceilings_library_exports():
+    """The benchmark's ceiling probes (libfp8ceilings.so, built beside the
+    library) load without a GPU and export their four entry points; the MFMA
+    probe rejects a block size it cannot run before launching anything."""
+    import ctypes
+    path = os.path.join(ROOT, "fp8_mixed_precision_amax_amd", "libfp8ceilings.so")
+    if not os.path.exists(path):
+        pytest.skip("libfp8ceilings.so not built")
+    C = ctypes.CDLL(path)
+    for n in ("fp8c_hbm_read", "fp8c_hbm_write", "fp8c_hbm_copy", "fp8c_mfma"):
+        assert hasattr(C, n), n
+    C.fp8c_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.c_void_p]
+    assert C.fp8c_mfma(1, 100, 1, None, None, None) != 0
