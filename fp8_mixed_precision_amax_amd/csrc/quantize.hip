@@ -114,15 +114,15 @@ __device__ __forceinline__ uint4 amax_ld(const uint4* p) {
 }
 
 template <int ACT, bool STREAM>
-__global__ __launch_bounds__(kAmaxThreads) void act_amax_kernel(const uint4* __restrict__ x,
+__global__ __launch_bounds__(kAmaxStreamThreads) void act_amax_kernel(const uint4* __restrict__ x,
                                                                 const uint4* __restrict__ x2, int64_t n16,
                                                                 uint16_t* __restrict__ partial, const void* gtab) {
     __shared__ __align__(16) uint32_t tab[act_table_bytes<ACT>() / 4];
     act_table_to_lds(tab, gtab, sizeof(tab));
     __syncthreads();
     uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
-    int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     for (; i + 3 * stride < n16; i += 4 * stride) {
         uint4 v[4], u[4];
 #pragma unroll
@@ -552,7 +552,7 @@ hipError_t launch_act_quantize(const QuantizeLaunch& q, CastArgs& a, hipStream_t
         const uint4* x = static_cast<const uint4*>(q.x);
         const uint4* x2 = static_cast<const uint4*>(q.x2);
 #define FP8K_AMAX(A, S) \
-    hipLaunchKernelGGL((act_amax_kernel<A, S>), dim3((unsigned)g), dim3(kAmaxThreads), 0, stream, x, x2, n16, \
+    hipLaunchKernelGGL((act_amax_kernel<A, S>), dim3((unsigned)g), dim3(kAmaxStreamThreads), 0, stream, x, x2, n16, \
                        q.partial, a.act_tab)
         if (q.act == 1) {
             if (big) FP8K_AMAX(1, true); else FP8K_AMAX(1, false);
