@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_PREFIX", "WRITE_PREFIX"),
                     help="per-stage HBM bytes per launch from a FETCH_SIZE and a WRITE_SIZE counter run "
                          "(each with --copy-reference), one line per stage, and exit")
+    ap.add_argument("--mfma", metavar="PREFIX",
+                    help="matrix-core utilisation of every GEMM launch of a counter run "
+                         "(--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F8), grouped by kernel and shape, and exit")
     return ap.parse_args()
 
 
@@ -176,6 +179,60 @@ def traffic(fetch_prefix, write_prefix, steps, warmup):
     digest = source_digest()
     for stage, v in per.items():
         print("%s %d %s" % (stage, round(sum(v) / len(v)), digest))
+
+
+# GEMM shapes (I, J, K) the bench launches: the headline step's, then the
+# other workloads' (N x M x K forward, N x K x M data gradient, M x K x N
+# weight gradient)
+def _bench_gemm_shapes():
+    lin = [(131072, 512, 2048), (131072, 2048, 512), (131072, 512, 8192), (16384, 8192, 8192),
+           (262144, 512, 8192), (8192, 8192, 16384)]
+    out = []
+    for N, K, M in lin[:-1]:
+        out += [(N, M, K), (N, K, M), (M, K, N)]
+    out.append(lin[-1])
+    return sorted(set(out))
+
+
+def mfma_summary(prefix, steps, warmup):
+    """Matrix-core utilisation of the GEMM launches of a counter run with
+    MfmaUtil (100 x MFMA-busy SIMD cycles / (active GPU cycles x SIMDs)) and
+    SQ_INSTS_VALU_MFMA_MOPS_F8 (FP8 matrix work in units of 512 FLOP): the
+    GEMM calls of the timed tensorwise and block-scaled steps by stage, then
+    every other GEMM launch grouped by kernel and FLOP count."""
+    by = collections.OrderedDict()
+    for r in csv.DictReader(open(prefix + "_counter_collection.csv")):
+        d = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    disp = [(kernel_kind(d["name"]), short_name(d["name"]), d) for _, d in sorted(by.items())
+            if kernel_kind(d["name"])]
+    used = set()
+    print("| recipe | stage | kernel | MFMA busy % (mean over the timed steps) | FLOP per launch (counter) |")
+    print("|---|---|---|---:|---:|")
+    for recipe in ("tensor", "block"):
+        per = collections.OrderedDict()
+        for st in walk_steps(disp, steps, warmup, recipe):
+            for stage, kind, name, d in st:
+                if kind == "gemm":
+                    per.setdefault((stage, name), []).append(d)
+                    used.add(id(d))
+        for (stage, name), ds in per.items():
+            print("| %s | %s | %s | %.1f | %.4g |" % (recipe, stage, name, sum(x["MfmaUtil"] for x in ds) / len(ds),
+                                                    ds[0]["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512))
+    shapes = _bench_gemm_shapes()
+    groups = collections.OrderedDict()
+    for kind, name, d in disp:
+        if kind != "gemm" or id(d) in used:
+            continue
+        flops = d["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512
+        match = [sh for sh in shapes if abs(2 * sh[0] * sh[1] * sh[2] - flops) <= 1e-6 * flops]
+        tag = "%.4g (%s)" % (flops, ", ".join("%dx%dx%d" % sh for sh in match) if match else "?")
+        groups.setdefault((name, tag), []).append(d["MfmaUtil"])
+    print()
+    print("| kernel | FLOP per launch (GEMMs of the bench with that count, I x J x K) | launches | MFMA busy % mean | min | max |")
+    print("|---|---|---:|---:|---:|---:|")
+    for (name, tag), v in groups.items():
+        print("| %s | %s | %d | %.1f | %.1f | %.1f |" % (name, tag, len(v), sum(v) / len(v), min(v), max(v)))
 
 
 def summarize(prefix, steps, warmup, recipe="tensor"):
@@ -824,6 +881,9 @@ def main():
         return
     if args.traffic:
         traffic(args.traffic[0], args.traffic[1], args.steps, args.warmup)
+        return
+    if args.mfma:
+        mfma_summary(args.mfma, args.steps, args.warmup)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
