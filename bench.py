@@ -440,7 +440,11 @@ def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8
     512 -> 2048 (GELU) -> 512, `mbs` microbatches of N tokens per cycle, the
     GELU fused into the quantizers.  Timed over `cycles` cycles (one untimed
     first) with the weight cache (W quantized on microbatch 1, reused on the
-    rest) and without it (W requantized every microbatch)."""
+    rest), without it (W requantized every microbatch), and, tensorwise, with
+    the cache and the amax hand-off on the edges without a GELU between
+    (block p's output is block p+1's input; block p+1's input gradient is
+    block p's output gradient).  The weight gradients of the last cycle are
+    compared bitwise across the runs."""
     d, h = 512, 2048
     R = fp8.RECIPE_BLOCK if recipe == "block" else fp8.RECIPE_TENSOR
     g = torch.Generator(device=dev)
@@ -452,29 +456,36 @@ def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8
     xs = [synth.normal_bf16((N, d), 1.0, g, device=dev) for _ in range(mbs)]
     dys = [synth.normal_bf16((N, d), 1e-3, g, device=dev) for _ in range(mbs)]
     shapes = [(d, h), (h, d)] * layers
-    res = {}
-    for cached in (True, False):
+    modes = [("cached", True, False), ("uncached", False, False)]
+    if recipe == "tensor":
+        modes.append(("cached_handoff", True, True))
+    res, final = {}, {}
+    for mode, cached, handoff in modes:
         lins = [fp8.Fp8Linear(N, K, M, R, device=dev, cache=cached) for K, M in shapes]
         pre = [torch.empty((N, h), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
         hid = [torch.empty((N, d), dtype=torch.bfloat16, device=dev) for _ in range(layers)]
         dws = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for K, M in shapes]
         dg = torch.empty((N, h), dtype=torch.bfloat16, device=dev)
         dh = [torch.empty((N, d), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        pa, pb = (fp8.amax_partials(dev), fp8.amax_partials(dev)) if handoff else (None, None)
 
         def cycle():
             for mb in range(mbs):
                 flag = (mb == 0) if cached else None
                 x = xs[mb]
                 for p in range(layers):
-                    lins[2 * p].forward(x, weights[2 * p], y=pre[p], is_first_microbatch=flag)
+                    lins[2 * p].forward(x, weights[2 * p], y=pre[p], is_first_microbatch=flag,
+                                        x_amax=pa if (handoff and p > 0) else None)
                     lins[2 * p + 1].forward(pre[p], weights[2 * p + 1], y=hid[p], is_first_microbatch=flag,
-                                            gelu=True)
+                                            gelu=True, y_amax=pa if (handoff and p + 1 < layers) else None)
                     x = hid[p]
                 g_in = dys[mb]
                 for p in reversed(range(layers)):
-                    lins[2 * p + 1].backward(g_in, dx=dg, dw=dws[2 * p + 1])
+                    lins[2 * p + 1].backward(g_in, dx=dg, dw=dws[2 * p + 1],
+                                             dy_amax=pb if (handoff and p + 1 < layers) else None)
                     out = dh[p & 1]
-                    lins[2 * p].backward(dg, dx=out, dw=dws[2 * p], gelu_input=pre[p])
+                    lins[2 * p].backward(dg, dx=out, dw=dws[2 * p], gelu_input=pre[p],
+                                         dx_amax=pb if (handoff and p > 0) else None)
                     g_in = out
         cycle()
         torch.cuda.synchronize()
@@ -484,16 +495,24 @@ def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8
             cycle()
         e1.record()
         torch.cuda.synchronize()
-        res[cached] = e0.elapsed_time(e1) / cycles
-        del lins, pre, hid, dws, dg, dh
+        res[mode] = e0.elapsed_time(e1) / cycles
+        final[mode] = [w.clone() for w in dws]
+        del lins, pre, hid, dws, dg, dh, pa, pb
         torch.cuda.empty_cache()
     flops = mbs * sum(6 * N * K * M for K, M in shapes)
-    return {"workload": "%d x (512->2048, GELU, 2048->512), N=%d per microbatch, %d microbatches per cycle, %s"
-                        % (layers, N, mbs, "tensorwise" if recipe == "tensor" else "1x128 / 128x128 blocks"),
-            "ms_per_cycle_cached": round(res[True], 3), "ms_per_cycle_uncached": round(res[False], 3),
-            "value_cached": round(flops / (res[True] / 1e3) / 1e12, 2),
-            "value_uncached": round(flops / (res[False] / 1e3) / 1e12, 2), "unit": "TFLOP/s",
-            "cache_speedup": round(res[False] / res[True], 4)}
+    out = {"workload": "%d x (512->2048, GELU, 2048->512), N=%d per microbatch, %d microbatches per cycle, %s"
+                       % (layers, N, mbs, "tensorwise" if recipe == "tensor" else "1x128 / 128x128 blocks"),
+           "ms_per_cycle_cached": round(res["cached"], 3), "ms_per_cycle_uncached": round(res["uncached"], 3),
+           "value_cached": round(flops / (res["cached"] / 1e3) / 1e12, 2),
+           "value_uncached": round(flops / (res["uncached"] / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+           "cache_speedup": round(res["uncached"] / res["cached"], 4),
+           "dw_cached_equals_uncached": all(torch.equal(a, b) for a, b in zip(final["cached"], final["uncached"]))}
+    if "cached_handoff" in res:
+        out["ms_per_cycle_cached_handoff"] = round(res["cached_handoff"], 3)
+        out["value_cached_handoff"] = round(flops / (res["cached_handoff"] / 1e3) / 1e12, 2)
+        out["dw_handoff_equals_cached"] = all(torch.equal(a, b)
+                                              for a, b in zip(final["cached_handoff"], final["cached"]))
+    return out
 
 
 def _amd_smi_sample():
@@ -975,8 +994,10 @@ def main():
         configs = config_times(fp8, torch, synth, args.steps, args.warmup, args.reps, dev)
         stack = {r: mlp_stack_times(fp8, torch, synth, N, 2, dev, r) for r in ("tensor", "block")}
         for r, v in stack.items():
-            print("MLP stack (%s): %.3f ms/cycle cached, %.3f uncached" %
-                  (r, v["ms_per_cycle_cached"], v["ms_per_cycle_uncached"]), file=sys.stderr, flush=True)
+            print("MLP stack (%s): %.3f ms/cycle cached, %.3f uncached%s" %
+                  (r, v["ms_per_cycle_cached"], v["ms_per_cycle_uncached"],
+                   ", %.3f cached with the amax hand-off" % v["ms_per_cycle_cached_handoff"]
+                   if "ms_per_cycle_cached_handoff" in v else ""), file=sys.stderr, flush=True)
     ceil = None
     if not args.no_block and not args.no_ceilings:
         ceil = ceilings(fp8, torch, synth, dev)
