@@ -905,7 +905,7 @@ def main():
         mfma_summary(args.mfma, args.steps, args.warmup)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch
