@@ -29,8 +29,10 @@
 //    after its last MFMA; the two B fragments alternate between two register
 //    sets).  The first half reads the second half of the same rows; the
 //    second half starts with the hand-off of the next stage and reads its
-//    first half, and right after the barrier the wave issues the DMA of the
-//    stage after that into the buffer just consumed.
+//    first half, and after the barrier the wave issues the DMA of the stage
+//    after that into the buffer just consumed, in four chunks of one A and
+//    one B block, one before each MFMA group of that half step (all eight at
+//    once after the barrier: 8192^3 423 -> 398-404 us with the spread).
 //  - the hand-off of a stage is one s_waitcnt vmcnt(n) on the wave's own DMA
 //    (n counted exactly: the epilogue stores issued after it) plus the
 //    barrier; fragment reads are inline assembly so the compiler adds no
@@ -150,19 +152,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     if (l_ok) set_load_item();
     const uint32_t smem0 = lds_off(smem);
     uint32_t dma_off = 0;   // stage buffer the next DMA fills
-    auto issue_stage = [&]() __attribute__((always_inline)) {
+    // DMA of one stage in four chunks (A block c and B block c), so they can be
+    // spread between matrix instructions; advance_stage() moves the load
+    // cursor once all four are issued
+    auto dma_chunk = [&](int c) __attribute__((always_inline)) {
         const uint32_t dA = smem0 + dma_off + (uint32_t)(wave * LA * 1024);
         const uint32_t dB = smem0 + dma_off + (uint32_t)(A_BYTES + wave * LB * 1024);
-#pragma unroll
-        for (int p = 0; p < LA; p++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(uintptr_t)(dA + p * 1024),
-                                                     16, (p & 1) ? loff1 : loff0,
-                                                     __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * KR), 0, 0);
-#pragma unroll
-        for (int p = 0; p < LB; p++)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(uintptr_t)(dB + p * 1024),
-                                                     16, (p & 1) ? loff1 : loff0,
-                                                     __builtin_amdgcn_readfirstlane(l_so + (uint32_t)p * KR), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(uintptr_t)(dA + c * 1024),
+                                                 16, (c & 1) ? loff1 : loff0,
+                                                 __builtin_amdgcn_readfirstlane(l_so + (uint32_t)c * KR), 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(uintptr_t)(dB + c * 1024),
+                                                 16, (c & 1) ? loff1 : loff0,
+                                                 __builtin_amdgcn_readfirstlane(l_so + (uint32_t)c * KR), 0, 0);
+    };
+    auto advance_stage = [&]() __attribute__((always_inline)) {
         dma_off = (dma_off + STAGE) & (S * STAGE - 1);
         l_so += BK;
         if (--l_left == 0) {
@@ -177,6 +180,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
                 l_left = 1;
             }
         }
+    };
+    auto issue_stage = [&]() __attribute__((always_inline)) {
+        dma_chunk(0);
+        dma_chunk(1);
+        dma_chunk(2);
+        dma_chunk(3);
+        advance_stage();
     };
 
     // ---- prologue: both stages in flight, stage 0 landed, the fragments of
@@ -302,22 +312,26 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
         acc[MI][0] = mfma<FA, FB>(FBC[0], fa[MI], (FIRST) ? vzero : acc[MI][0]);                  \
         acc[MI][1] = mfma<FA, FB>(FBC[1], fa[MI], (FIRST) ? vzero : acc[MI][1]);                  \
     } while (0)
-#define FP8K_HALF(FBC, FBN, FIRST, A0, B0)                                                         \
+#define FP8K_HALF(FBC, FBN, FIRST, A0, B0, DMA)                                                    \
     do {                                                                                           \
         const uint32_t a0_ = (A0), a1_ = a0_ ^ 16u, b0_ = (B0), b1_ = b0_ ^ 16u;                   \
+        if (DMA) dma_chunk(0);                                                                     \
         FP8K_MF(0, FBC, FIRST);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         fa[0] = ds_frag<0>(a0_, a1_);                                                              \
         FBN[0] = ds_frag<0>(b0_, b1_);                                                             \
+        if (DMA) dma_chunk(1);                                                                     \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         FP8K_MF(1, FBC, FIRST);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         fa[1] = ds_frag<4096>(a0_, a1_);                                                           \
         FBN[1] = ds_frag<4096>(b0_, b1_);                                                          \
+        if (DMA) dma_chunk(2);                                                                     \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         FP8K_MF(2, FBC, FIRST);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         fa[2] = ds_frag<8192>(a0_, a1_);                                                           \
+        if (DMA) dma_chunk(3);                                                                     \
         __builtin_amdgcn_sched_barrier(0);                                                         \
         FP8K_MF(3, FBC, FIRST);                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                         \
@@ -330,16 +344,16 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
                      : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb0[0]), "+v"(fb0[1]) \
                      :                                                                             \
                      : "memory");                                                                  \
-        FP8K_HALF(fb0, fb1, FIRST, (smem0 + cur_off + offA) ^ 64u, (smem0 + cur_off + offB) ^ 64u);  \
+        FP8K_HALF(fb0, fb1, FIRST, (smem0 + cur_off + offA) ^ 64u, (smem0 + cur_off + offB) ^ 64u, false); \
         wait_vm_n(st_cur);                                                                         \
         st_cur = 0;                                                                                \
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"                                           \
                      : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb1[0]), "+v"(fb1[1]) \
                      :                                                                             \
                      : "memory");                                                                  \
-        issue_stage();                                                                             \
         cur_off ^= (uint32_t)STAGE;                                                                \
-        FP8K_HALF(fb1, fb0, false, smem0 + cur_off + offA, smem0 + cur_off + offB);                \
+        FP8K_HALF(fb1, fb0, false, smem0 + cur_off + offA, smem0 + cur_off + offB, true);          \
+        advance_stage();                                                                           \
     } while (0)
 
     const v16f vzero = {};
