@@ -70,21 +70,27 @@ def parse():
 
 
 SHAPES = [(512, 2048), (2048, 512)]
-KINDS = (("amax_partial_kernel", "amax"), ("cast_kernel", "cast"), ("gemm_block_kernel", "gemm"),
+KINDS = (("amax_partial_kernel", "amax"), ("amax_pair_kernel", "amax"), ("cast_kernel", "cast"),
+         ("cast_pair_kernel", "cast"), ("gemm_block_kernel", "gemm"),
          ("gemm_block_wide_kernel", "gemm"), ("gemm_tensor_kernel", "gemm"), ("splitk_reduce_kernel", "reduce"))
 COPY_BYTES = 2 * 512 * 1024 * 1024      # the --copy-reference kernel reads 512 MiB and writes 512 MiB
 
 
 def step_sequence(shapes, recipe="tensor"):
-    """Library calls of one step, in launch order, with the kernels each
-    launches (weight requantized every step; a tensorwise quantize runs the
-    amax pass then the cast, a block-scaled one the cast alone)."""
+    """Library kernels of one step, in launch order, grouped by stage (weight
+    requantized every step; a tensorwise quantize runs the amax pass then the
+    cast, a block-scaled one the cast alone).  Tensorwise, the forward pass
+    quantizes X and W together: one amax launch and one cast launch for both
+    (stage quant_xw)."""
     q = ("cast",) if recipe == "block" else ("amax", "cast")
     seq = []
     for K, M in shapes:
         tag = "%dx%d" % (K, M)
-        seq += [("quant_w_" + tag, q), ("quant_x_" + tag, q),
-                ("gemm_fprop_" + tag, ("gemm",)), ("quant_dy_" + tag, q),
+        if recipe == "block":
+            seq += [("quant_w_" + tag, q), ("quant_x_" + tag, q)]
+        else:
+            seq += [("quant_xw_" + tag, q)]
+        seq += [("gemm_fprop_" + tag, ("gemm",)), ("quant_dy_" + tag, q),
                 ("gemm_dgrad_" + tag, ("gemm",)), ("gemm_wgrad_" + tag, ("gemm",))]
     return seq
 
@@ -308,7 +314,9 @@ def stage_times(fp8, torch, layers, reps, recipe="tensor"):
     with an event recorded between consecutive calls on the stream the kernels
     run on (torch's current stream).  Each call thus runs after the call that
     precedes it in a real step (e.g. a quantize reads while the previous
-    GEMM's output drains to HBM).  Returns (stages, ms per instrumented step)."""
+    GEMM's output drains to HBM).  One difference: the tensorwise forward
+    quantizes X and W in shared launches, while here they are two calls, so
+    each can be timed.  Returns (stages, ms per instrumented step)."""
     E4, E5 = fp8.E4M3, fp8.E5M2
     block = recipe == "block"
     act = fp8.SCALE_1x128 if block else fp8.SCALE_TENSOR

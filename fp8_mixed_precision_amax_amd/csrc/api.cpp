@@ -110,9 +110,9 @@ fp8_status hip_status(hipError_t e, const char* what) {
 // given_amax: tensorwise only, the amax partials of x from its producer (the
 // amax pass is skipped); otherwise ws holds the pass's partials
 // act: 0 quantize x; 1 quantize GELU(x); 2 quantize dGELU(x, x2)
-fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, int scaling, unsigned layouts,
-                       const fp8_qtensor* out, void* ws, hipStream_t st, const void* given_amax = nullptr,
-                       int act = 0, const void* x2 = nullptr) {
+static fp8k::QuantizeLaunch quantize_launch(const void* x, int64_t rows, int64_t cols, int format, int scaling,
+                                            unsigned layouts, const fp8_qtensor* out, void* ws,
+                                            const void* given_amax, int act, const void* x2) {
     fp8k::QuantizeLaunch q;
     q.x = x;
     q.rows = rows;
@@ -132,7 +132,28 @@ fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, in
     q.hist_len = 0;
     q.act = act;
     q.x2 = x2;
+    return q;
+}
+
+fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, int scaling, unsigned layouts,
+                       const fp8_qtensor* out, void* ws, hipStream_t st, const void* given_amax = nullptr,
+                       int act = 0, const void* x2 = nullptr) {
+    const fp8k::QuantizeLaunch q = quantize_launch(x, rows, cols, format, scaling, layouts, out, ws, given_amax, act, x2);
     return hip_status(fp8k::launch_quantize(q, st), "quantize launch");
+}
+
+// Two tensorwise E4M3 quantizes of plain inputs, both layouts, in one amax
+// launch and one cast launch (a layer's input and its weight); each tensor's
+// amax partials go to its own 4 KiB buffer.
+static fp8_status do_quantize_pair(const void* xa, int64_t ra, int64_t ca, const fp8_qtensor* outa, void* wsa,
+                                   const void* xb, int64_t rb, int64_t cb, const fp8_qtensor* outb, void* wsb,
+                                   hipStream_t st) {
+    const unsigned both = FP8_LAYOUT_ROW | FP8_LAYOUT_COL;
+    const fp8k::QuantizeLaunch qa = quantize_launch(xa, ra, ca, FP8_E4M3, FP8_SCALE_TENSOR, both, outa, wsa, nullptr, 0,
+                                                    nullptr);
+    const fp8k::QuantizeLaunch qb = quantize_launch(xb, rb, cb, FP8_E4M3, FP8_SCALE_TENSOR, both, outb, wsb, nullptr, 0,
+                                                    nullptr);
+    return hip_status(fp8k::launch_quantize_pair(qa, qb, st), "quantize launch");
 }
 
 fp8k::GemmScale tensor_scale(const float* sinv) { return fp8k::GemmScale{sinv, 0, 0, 0}; }
@@ -453,15 +474,20 @@ static fp8_status linear_fwd(const void* x, int act, const void* w, int64_t N, i
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     void* gws = wsb + kPartialBytes;
     const size_t gws_bytes = ws_bytes - kPartialBytes;
-    if (flag != 0) {
-        FP8_TRY(do_quantize(w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, wq, ws, st));
-        if (flag == 1) {
-            cache->valid = 1;
-            cache->fills++;
-        }
+    if (flag != 0 && recipe == FP8_RECIPE_TENSOR && act == 0 && !x_amax_partials && gws_bytes >= kPartialBytes) {
+        // X and W together: one amax launch and one cast launch; W's partials
+        // borrow the GEMM workspace, which the forward GEMM only uses after
+        FP8_TRY(do_quantize_pair(x, N, K, saved_x, ws, w, M, K, wq, gws, st));
+    } else {
+        if (flag != 0)
+            FP8_TRY(do_quantize(w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, wq, ws, st));
+        FP8_TRY(do_quantize(x, N, K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x, ws, st,
+                            x_amax_partials, act));
     }
-    FP8_TRY(do_quantize(x, N, K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x, ws, st, x_amax_partials,
-                        act));
+    if (flag == 1) {
+        cache->valid = 1;
+        cache->fills++;
+    }
     if (recipe == FP8_RECIPE_TENSOR)
         return do_gemm(saved_x->q_row, FP8_E4M3, tensor_scale(saved_x->scale_inv), wq->q_row, FP8_E4M3,
                        tensor_scale(wq->scale_inv), N, M, K, y, gws, gws_bytes, st, y_amax_partials);

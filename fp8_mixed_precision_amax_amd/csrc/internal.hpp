@@ -34,6 +34,9 @@ struct QuantizeLaunch {
 
 int amax_partial_count(int64_t numel);
 hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream);
+// two tensorwise quantizes, same format, no transform, amax pass included
+// (partial_given false), each with its own partials buffer
+hipError_t launch_quantize_pair(const QuantizeLaunch& qa, const QuantizeLaunch& qb, hipStream_t stream);
 
 // GELU tables of the current device (gelu.hip): built on first use, which
 // waits for them and cannot be captured into a graph.

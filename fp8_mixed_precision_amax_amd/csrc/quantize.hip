@@ -55,7 +55,8 @@ constexpr int kAmaxStreamThreads = 1024;   // the streamed sweep: 4x the threads
 // of the threads' packed magnitude maxima m goes to partial[blockIdx.x], and
 // workgroup 0 zero-fills the unused tail of the kMaxAmaxPartials slots so
 // readers may scan all of them.
-__device__ __forceinline__ void amax_store_partial(uint32_t m, uint16_t* __restrict__ partial) {
+__device__ __forceinline__ void amax_store_partial(uint32_t m, uint16_t* __restrict__ partial, int block,
+                                                   int nblocks) {
     m = wave_max_u32(hmax_u16(m));
     __shared__ uint32_t red[kAmaxStreamThreads / 64];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -63,10 +64,13 @@ __device__ __forceinline__ void amax_store_partial(uint32_t m, uint16_t* __restr
     if (threadIdx.x == 0) {
         uint32_t r = red[0];
         for (int w = 1; w < (int)(blockDim.x >> 6); w++) r = r > red[w] ? r : red[w];
-        partial[blockIdx.x] = (uint16_t)r;
+        partial[block] = (uint16_t)r;
     }
-    if (blockIdx.x == 0)
-        for (int p = (int)gridDim.x + threadIdx.x; p < kMaxAmaxPartials; p += (int)blockDim.x) partial[p] = 0;
+    if (block == 0)
+        for (int p = nblocks + threadIdx.x; p < kMaxAmaxPartials; p += (int)blockDim.x) partial[p] = 0;
+}
+__device__ __forceinline__ void amax_store_partial(uint32_t m, uint16_t* __restrict__ partial) {
+    amax_store_partial(m, partial, (int)blockIdx.x, (int)gridDim.x);
 }
 
 __device__ __forceinline__ uint32_t mag8_max(uint32_t m, uint4 v) {
@@ -80,12 +84,13 @@ __device__ __forceinline__ uint32_t mag8_max(uint32_t m, uint4 v) {
 // (the cast gains nothing from the cache: measured) and is streamed with
 // four non-temporal loads in flight per thread: with one, the grid keeps
 // about 8 MiB of reads outstanding, half of what HBM's latency needs.
+// The packed magnitude maximum of this thread's share of x when `nblocks`
+// workgroups sweep it and this one is number `block`.
 template <bool STREAM>
-__global__ __launch_bounds__(kAmaxStreamThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
-                                                                          uint16_t* __restrict__ partial) {
+__device__ __forceinline__ uint32_t amax_sweep(const uint4* __restrict__ x, int64_t n16, int block, int nblocks) {
     uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)nblocks * blockDim.x;
+    int64_t i = (int64_t)block * blockDim.x + threadIdx.x;
     if constexpr (STREAM) {
         for (; i + 3 * stride < n16; i += 4 * stride) {
             uint4 v[4];
@@ -96,7 +101,26 @@ __global__ __launch_bounds__(kAmaxStreamThreads) void amax_partial_kernel(const 
         }
     }
     for (; i < n16; i += stride) m = mag8_max(m, x[i]);
-    amax_store_partial(m, partial);
+    return m;
+}
+
+template <bool STREAM>
+__global__ __launch_bounds__(kAmaxStreamThreads) void amax_partial_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                                          uint16_t* __restrict__ partial) {
+    amax_store_partial(amax_sweep<STREAM>(x, n16, (int)blockIdx.x, (int)gridDim.x), partial);
+}
+
+// Pass 1 of two tensorwise quantizes in one launch (a layer's input and its
+// weight): workgroups [0, ga) sweep a, the rest sweep b, each part writing
+// its own partials as a launch of its own would.
+template <bool STREAM_A>
+__global__ __launch_bounds__(kAmaxStreamThreads) void amax_pair_kernel(const uint4* __restrict__ xa, int64_t na16,
+                                                                       uint16_t* __restrict__ pa, int ga,
+                                                                       const uint4* __restrict__ xb, int64_t nb16,
+                                                                       uint16_t* __restrict__ pb) {
+    const int b = (int)blockIdx.x;
+    if (b < ga) amax_store_partial(amax_sweep<STREAM_A>(xa, na16, b, ga), pa, b, ga);
+    else amax_store_partial(amax_sweep<false>(xb, nb16, b - ga, (int)gridDim.x - ga), pb, b - ga, (int)gridDim.x - ga);
 }
 
 // Table bytes of an activation: the bf16 GELU table (ACT 1) or the fp32 GELU'
@@ -473,6 +497,19 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     cast_tile<FMT, MODE, 0>(a, slot, nullptr);
 }
 
+// The casts of two tensorwise quantizes in one launch: workgroups [0, ga)
+// take a's tiles (four per workgroup), the rest b's.
+template <int FMT>
+__global__ __launch_bounds__(256) void cast_pair_kernel(CastArgs a, int ga, CastArgs b) {
+    const bool first = (int)blockIdx.x < ga;
+    const CastArgs& c = first ? a : b;
+    const int64_t ntiles = (c.R >> 7) * (c.C >> 7);
+    const int64_t slot = (int64_t)((int)blockIdx.x - (first ? 0 : ga)) * 4 + (threadIdx.x >> 6);
+    if (slot >= ntiles) return;
+    if (first) cast_tile<FMT, 0, 0>(a, slot, nullptr);
+    else cast_tile<FMT, 0, 0>(b, slot, nullptr);
+}
+
 // MODE 0 or 1 on GELU(x) / dGELU(x, x2): the table goes to LDS once per
 // workgroup.  Tensorwise, the workgroup's waves then take tiles in turn; in
 // 1x128 blocks each wave takes one tile (in a loop the compiler interleaves
@@ -583,7 +620,7 @@ hipError_t launch_act_quantize(const QuantizeLaunch& q, CastArgs& a, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
+static CastArgs cast_args(const QuantizeLaunch& q) {
     CastArgs a;
     a.x = static_cast<const uint16_t*>(q.x);
     a.R = q.rows;
@@ -602,6 +639,11 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
     a.x2 = static_cast<const uint16_t*>(q.x2);
     a.act_tab = nullptr;
     a.row_cached = q.rows * q.cols <= (int64_t(128) << 20);
+    return a;
+}
+
+hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
+    CastArgs a = cast_args(q);
     if (q.act) return launch_act_quantize(q, a, stream);
     if (q.scaling == 0 && !q.partial_given) {
         const int g = amax_partial_count(q.rows * q.cols);
@@ -640,6 +682,42 @@ hipError_t launch_quantize(const QuantizeLaunch& q, hipStream_t stream) {
         hipLaunchKernelGGL(history_update_kernel, dim3(1), dim3(256), 0, stream, q.partial, ntiles, q.hist,
                            q.hist_len, q.amax);
     }
+    return hipGetLastError();
+}
+
+}  // namespace fp8k
+
+namespace fp8k {
+
+// Two tensorwise quantizes (same format, plain input, amax pass included)
+// as one amax launch and one cast launch: a layer's input x (a) and its
+// weight (b), whose separate launches would each leave the GPU mostly idle
+// for a small tensor.  The bytes written are those of two launch_quantize
+// calls.
+hipError_t launch_quantize_pair(const QuantizeLaunch& qa, const QuantizeLaunch& qb, hipStream_t stream) {
+    const int64_t na16 = qa.rows * qa.cols / 8, nb16 = qb.rows * qb.cols / 8;
+    const int ga = amax_partial_count(qa.rows * qa.cols);
+    int64_t gb = (nb16 + kAmaxStreamThreads - 1) / kAmaxStreamThreads;
+    if (gb > 512) gb = 512;
+    if (gb < 1) gb = 1;
+    const dim3 agrid((unsigned)(ga + gb));
+    if (qa.rows * qa.cols * 2 > (int64_t(256) << 20))
+        hipLaunchKernelGGL(amax_pair_kernel<true>, agrid, dim3(kAmaxStreamThreads), 0, stream,
+                           static_cast<const uint4*>(qa.x), na16, qa.partial, ga, static_cast<const uint4*>(qb.x),
+                           nb16, qb.partial);
+    else
+        hipLaunchKernelGGL(amax_pair_kernel<false>, agrid, dim3(kAmaxStreamThreads), 0, stream,
+                           static_cast<const uint4*>(qa.x), na16, qa.partial, ga, static_cast<const uint4*>(qb.x),
+                           nb16, qb.partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const CastArgs a = cast_args(qa), b = cast_args(qb);
+    const int64_t ta = (qa.rows / 128) * (qa.cols / 128), tb = (qb.rows / 128) * (qb.cols / 128);
+    const int wa = (int)((ta + 3) / 4), wb = (int)((tb + 3) / 4);
+    if (qa.format == 0)
+        hipLaunchKernelGGL((cast_pair_kernel<0>), dim3((unsigned)(wa + wb)), dim3(256), 0, stream, a, wa, b);
+    else
+        hipLaunchKernelGGL((cast_pair_kernel<1>), dim3((unsigned)(wa + wb)), dim3(256), 0, stream, a, wa, b);
     return hipGetLastError();
 }
 

@@ -33,8 +33,9 @@ def test_walk_steps_assigns_every_dispatch_to_its_call():
     for i, st in enumerate(steps):
         for stage, kind, name, (s, orig) in st:
             assert s == i + 2 and orig == stage
-        # 2 layers x (3 two-kernel quantizes + 3 GEMMs + 1 split-K reduce)
-        assert len(st) == 2 * (3 * 2 + 3 + 1)
+        # 2 layers x (2 two-kernel quantizes (X with W, then dY) + 3 GEMMs
+        # + 1 split-K reduce)
+        assert len(st) == 2 * (2 * 2 + 3 + 1)
 
 
 def test_walk_steps_block_recipe_starts_at_the_first_weight_block_cast():
