@@ -110,17 +110,18 @@ __global__ __launch_bounds__(kAmaxStreamThreads) void amax_partial_kernel(const 
     amax_store_partial(amax_sweep<STREAM>(x, n16, (int)blockIdx.x, (int)gridDim.x), partial);
 }
 
-// Pass 1 of two tensorwise quantizes in one launch (a layer's input and its
-// weight): workgroups [0, ga) sweep a, the rest sweep b, each part writing
-// its own partials as a launch of its own would.
+// Pass 1 of two tensorwise quantizes in one launch (a layer's input a and
+// its weight b): workgroups [0, gb) sweep the small b first, so they run
+// beside a's rather than after them, the rest sweep a; each part writes its
+// own partials as a launch of its own would.
 template <bool STREAM_A>
 __global__ __launch_bounds__(kAmaxStreamThreads) void amax_pair_kernel(const uint4* __restrict__ xa, int64_t na16,
-                                                                       uint16_t* __restrict__ pa, int ga,
+                                                                       uint16_t* __restrict__ pa,
                                                                        const uint4* __restrict__ xb, int64_t nb16,
-                                                                       uint16_t* __restrict__ pb) {
+                                                                       uint16_t* __restrict__ pb, int gb) {
     const int b = (int)blockIdx.x;
-    if (b < ga) amax_store_partial(amax_sweep<STREAM_A>(xa, na16, b, ga), pa, b, ga);
-    else amax_store_partial(amax_sweep<false>(xb, nb16, b - ga, (int)gridDim.x - ga), pb, b - ga, (int)gridDim.x - ga);
+    if (b < gb) amax_store_partial(amax_sweep<false>(xb, nb16, b, gb), pb, b, gb);
+    else amax_store_partial(amax_sweep<STREAM_A>(xa, na16, b - gb, (int)gridDim.x - gb), pa, b - gb, (int)gridDim.x - gb);
 }
 
 // Table bytes of an activation: the bf16 GELU table (ACT 1) or the fp32 GELU'
@@ -497,17 +498,17 @@ __global__ __launch_bounds__(256) void cast_kernel(CastArgs a) {
     cast_tile<FMT, MODE, 0>(a, slot, nullptr);
 }
 
-// The casts of two tensorwise quantizes in one launch: workgroups [0, ga)
-// take a's tiles (four per workgroup), the rest b's.
+// The casts of two tensorwise quantizes in one launch: workgroups [0, gb)
+// take the small b's tiles (four per workgroup) first, the rest a's.
 template <int FMT>
-__global__ __launch_bounds__(256) void cast_pair_kernel(CastArgs a, int ga, CastArgs b) {
-    const bool first = (int)blockIdx.x < ga;
-    const CastArgs& c = first ? a : b;
+__global__ __launch_bounds__(256) void cast_pair_kernel(CastArgs a, CastArgs b, int gb) {
+    const bool small = (int)blockIdx.x < gb;
+    const CastArgs& c = small ? b : a;
     const int64_t ntiles = (c.R >> 7) * (c.C >> 7);
-    const int64_t slot = (int64_t)((int)blockIdx.x - (first ? 0 : ga)) * 4 + (threadIdx.x >> 6);
+    const int64_t slot = (int64_t)((int)blockIdx.x - (small ? 0 : gb)) * 4 + (threadIdx.x >> 6);
     if (slot >= ntiles) return;
-    if (first) cast_tile<FMT, 0, 0>(a, slot, nullptr);
-    else cast_tile<FMT, 0, 0>(b, slot, nullptr);
+    if (small) cast_tile<FMT, 0, 0>(b, slot, nullptr);
+    else cast_tile<FMT, 0, 0>(a, slot, nullptr);
 }
 
 // MODE 0 or 1 on GELU(x) / dGELU(x, x2): the table goes to LDS once per
@@ -703,21 +704,21 @@ hipError_t launch_quantize_pair(const QuantizeLaunch& qa, const QuantizeLaunch& 
     const dim3 agrid((unsigned)(ga + gb));
     if (qa.rows * qa.cols * 2 > (int64_t(256) << 20))
         hipLaunchKernelGGL(amax_pair_kernel<true>, agrid, dim3(kAmaxStreamThreads), 0, stream,
-                           static_cast<const uint4*>(qa.x), na16, qa.partial, ga, static_cast<const uint4*>(qb.x),
-                           nb16, qb.partial);
+                           static_cast<const uint4*>(qa.x), na16, qa.partial, static_cast<const uint4*>(qb.x), nb16,
+                           qb.partial, (int)gb);
     else
         hipLaunchKernelGGL(amax_pair_kernel<false>, agrid, dim3(kAmaxStreamThreads), 0, stream,
-                           static_cast<const uint4*>(qa.x), na16, qa.partial, ga, static_cast<const uint4*>(qb.x),
-                           nb16, qb.partial);
+                           static_cast<const uint4*>(qa.x), na16, qa.partial, static_cast<const uint4*>(qb.x), nb16,
+                           qb.partial, (int)gb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const CastArgs a = cast_args(qa), b = cast_args(qb);
     const int64_t ta = (qa.rows / 128) * (qa.cols / 128), tb = (qb.rows / 128) * (qb.cols / 128);
     const int wa = (int)((ta + 3) / 4), wb = (int)((tb + 3) / 4);
     if (qa.format == 0)
-        hipLaunchKernelGGL((cast_pair_kernel<0>), dim3((unsigned)(wa + wb)), dim3(256), 0, stream, a, wa, b);
+        hipLaunchKernelGGL((cast_pair_kernel<0>), dim3((unsigned)(wa + wb)), dim3(256), 0, stream, a, b, wb);
     else
-        hipLaunchKernelGGL((cast_pair_kernel<1>), dim3((unsigned)(wa + wb)), dim3(256), 0, stream, a, wa, b);
+        hipLaunchKernelGGL((cast_pair_kernel<1>), dim3((unsigned)(wa + wb)), dim3(256), 0, stream, a, b, wb);
     return hipGetLastError();
 }
 
