@@ -408,7 +408,11 @@ void fp8_wcache_destroy(fp8_wcache h) { std::free(h); }
 
 size_t fp8_linear_workspace_bytes(int64_t N, int64_t K, int64_t M, fp8_recipe recipe) {
     (void)recipe;
-    return kPartialBytes + linear_gemm_ws(N, K, M);
+    // the input's amax partials, then the GEMM workspace; the GEMM part is at
+    // least 4 KiB so that the forward can hold the weight's partials there
+    // while it quantizes input and weight together
+    const size_t g = linear_gemm_ws(N, K, M);
+    return kPartialBytes + (g > kPartialBytes ? g : kPartialBytes);
 }
 
 static fp8_status check_linear_common(int64_t N, int64_t K, int64_t M, int recipe, void* ws, size_t ws_bytes) {
@@ -474,9 +478,10 @@ static fp8_status linear_fwd(const void* x, int act, const void* w, int64_t N, i
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     void* gws = wsb + kPartialBytes;
     const size_t gws_bytes = ws_bytes - kPartialBytes;
-    if (flag != 0 && recipe == FP8_RECIPE_TENSOR && act == 0 && !x_amax_partials && gws_bytes >= kPartialBytes) {
+    if (flag != 0 && recipe == FP8_RECIPE_TENSOR && act == 0 && !x_amax_partials) {
         // X and W together: one amax launch and one cast launch; W's partials
-        // borrow the GEMM workspace, which the forward GEMM only uses after
+        // borrow the GEMM workspace (at least 4 KiB, checked above), which the
+        // forward GEMM only uses after
         FP8_TRY(do_quantize_pair(x, N, K, saved_x, ws, w, M, K, wq, gws, st));
     } else {
         if (flag != 0)

@@ -176,3 +176,30 @@ def test_full_size_512x2048_sampled(fp8):
         got = to_np_u16(out)[ii, jj]
         hw = mfma_window_bound(A, fa, B, fb, np.float32(sa * sb), ii, jj)
         check_bf16(got, ref, Kc, "full-size " + name, hw)
+
+
+def test_forward_weight_larger_than_input(fp8):
+    """A short microbatch against a large weight (N = 256, K = 2048,
+    M = 8192): the forward quantizes X and W together with W's part of the
+    launch at its workgroup cap and X's part small; both quantized tensors
+    bit-exact, 2048 sampled outputs of Y against the oracle; the forward with
+    the cache (W quantized alone on the second microbatch) gives the same Y."""
+    N, K, M = 256, 2048, 8192
+    g = torch.Generator().manual_seed(31)
+    x = synth.normal_bf16((N, K), 1.0, g)
+    w = synth.normal_bf16((M, K), 0.02, g)
+    lin = fp8.Fp8Linear(N, K, M, fp8.RECIPE_TENSOR, cache=True)
+    y = lin.forward(cuda_bf16(x), cuda_bf16(w), is_first_microbatch=True)
+    y2 = lin.forward(cuda_bf16(x), None, is_first_microbatch=False)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    xq = oracle.quant_tensor(synth.bits(x), "e4m3")
+    wq = oracle.quant_tensor(synth.bits(w), "e4m3")
+    check_q(lin.saved_x, xq, "tensor")
+    check_q(lin.weight_q(), wq, "tensor")
+    rng = np.random.default_rng(3)
+    ii = rng.integers(0, N, 2048)
+    jj = rng.integers(0, M, 2048)
+    ref = oracle.gemm_tensor_sampled(xq["q_row"], "e4m3", wq["q_row"], "e4m3", xq["scale_inv"], wq["scale_inv"], ii, jj)
+    hw = mfma_window_bound(xq["q_row"], "e4m3", wq["q_row"], "e4m3", np.float32(xq["scale_inv"] * wq["scale_inv"]), ii, jj)
+    check_bf16(to_np_u16(y)[ii, jj], ref, K, "weight-larger Y", hw)
