@@ -102,3 +102,10 @@ def test_amd_smi_sample_missing_tool(monkeypatch):
 
     monkeypatch.setattr(subprocess, "run", boom)
     assert bench._amd_smi_sample() is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr) and not r.stdout.strip().startswith("{")
