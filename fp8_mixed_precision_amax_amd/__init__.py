@@ -8,6 +8,7 @@ for device memory and the current stream only.
     gemm(a, b, ...)                    -> bf16 [I, J]
     Fp8Linear(M, K, recipe)            forward / backward with optional cache
 """
+import contextlib
 import ctypes
 
 import torch
@@ -33,6 +34,13 @@ def _ptr(t):
 def _stream(stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on(stream):
+    """Allocate temporaries (workspace, contiguous copies, outputs) on the
+    stream the library launches on: the caching allocator then reuses them
+    only after that stream's work, and any copy torch makes runs on it too."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
 
 
 def _dev(x):
@@ -91,6 +99,11 @@ def quantize(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=
     """Current-scaling FP8 quantization of a bf16 [rows, cols] device tensor.
     amax_partials (tensorwise only): x's amax partials from its producer
     (fp8_quantize_from_amax: the cast pass alone)."""
+    with _on(stream):
+        return _quantize(x, fmt, scaling, layouts, out, stream, amax_partials)
+
+
+def _quantize(x, fmt, scaling, layouts, out, stream, amax_partials):
     L = lib()
     if x.dtype != torch.bfloat16 or x.dim() != 2:
         raise ValueError("x must be a 2-D bfloat16 tensor")
@@ -117,6 +130,11 @@ def quantize_delayed(x, fmt, history, layouts=LAYOUT_ROW | LAYOUT_COL, out=None,
     """Delayed tensorwise scaling: encode with FMAX / max(history), then roll
     the fp32 device tensor `history` (most recent amax first) and store
     amax(x) in front.  Returns the QTensor (out.amax = amax(x))."""
+    with _on(stream):
+        return _quantize_delayed(x, fmt, history, layouts, out, stream)
+
+
+def _quantize_delayed(x, fmt, history, layouts, out, stream):
     L = lib()
     if x.dtype != torch.bfloat16 or x.dim() != 2:
         raise ValueError("x must be a 2-D bfloat16 tensor")
@@ -145,9 +163,10 @@ def _bf16_pair(name, *ts):
 def gelu(x, out=None, stream=None):
     """GELU(x) elementwise (exact erf form), bf16 in and out (fp8_gelu)."""
     _bf16_pair("gelu", x)
-    if out is None:
-        out = torch.empty_like(x)
-    _lib.check(lib().fp8_gelu(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        _lib.check(lib().fp8_gelu(_ptr(x), _ptr(out), x.numel(), _stream(stream)))
     return out
 
 
@@ -155,13 +174,19 @@ def dgelu(dy, x, out=None, stream=None):
     """dy * GELU'(x) elementwise, bf16 in and out (fp8_dgelu): dy is the
     gradient of GELU's output, x GELU's input."""
     _bf16_pair("dgelu", dy, x)
-    if out is None:
-        out = torch.empty_like(x)
-    _lib.check(lib().fp8_dgelu(_ptr(dy), _ptr(x), _ptr(out), x.numel(), _stream(stream)))
+    with _on(stream):
+        if out is None:
+            out = torch.empty_like(x)
+        _lib.check(lib().fp8_dgelu(_ptr(dy), _ptr(x), _ptr(out), x.numel(), _stream(stream)))
     return out
 
 
 def _act_quantize(name, fn, xs, fmt, scaling, layouts, out, stream):
+    with _on(stream):
+        return _act_quantize_on(name, fn, xs, fmt, scaling, layouts, out, stream)
+
+
+def _act_quantize_on(name, fn, xs, fmt, scaling, layouts, out, stream):
     L = lib()
     _bf16_pair(name, *xs)
     if xs[0].dim() != 2:
@@ -207,6 +232,11 @@ def gemm(a, fa, sa, b, fb, sb, out=None, stream=None, amax_out=None):
     """C[i][j] = bf16(sum_k A[i][k] B[j][k] * scales); a [I, K], b [J, K]
     uint8 FP8 codes; sa / sb are GemmScaleC (see gemm_scale).  amax_out
     (tensorwise only): receives C's amax partials (fp8_gemm_amax)."""
+    with _on(stream):
+        return _gemm(a, fa, sa, b, fb, sb, out, stream, amax_out)
+
+
+def _gemm(a, fa, sa, b, fb, sb, out, stream, amax_out):
     L = lib()
     I, K = a.shape
     J, K2 = b.shape
@@ -286,7 +316,8 @@ class Fp8Linear:
         quantize (fp8_linear_fwd_gelu; no x_amax)."""
         flag = -1 if is_first_microbatch is None else int(bool(is_first_microbatch))
         if y is None:
-            y = torch.empty((self.N, self.M), dtype=torch.bfloat16, device=x.device)
+            with _on(stream):
+                y = torch.empty((self.N, self.M), dtype=torch.bfloat16, device=x.device)
         cache = self.cache.handle if (self.cache is not None and flag != -1) else None
         if gelu:
             if x_amax is not None:
@@ -310,10 +341,11 @@ class Fp8Linear:
         gradient of GELU's output and the incoming gradient is
         dy * GELU'(gelu_input), applied by dY's quantize
         (fp8_linear_bwd_dgelu; no dy_amax)."""
-        if need_dx and dx is None:
-            dx = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dy.device)
-        if need_dw and dw is None:
-            dw = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dy.device)
+        with _on(stream):
+            if need_dx and dx is None:
+                dx = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dy.device)
+            if need_dw and dw is None:
+                dw = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dy.device)
         use_cache = self.cache is not None and getattr(self, "_last_flag", -1) != -1
         cache = self.cache.handle if use_cache else None
         dxp, dwp = (_ptr(dx) if need_dx else None), (_ptr(dw) if need_dw else None)

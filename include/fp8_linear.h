@@ -133,9 +133,9 @@ size_t fp8_quantize_workspace_bytes(int64_t rows, int64_t cols, fp8_scaling scal
  * Quantize a bf16 tensor x [rows, cols] to FP8 with current scaling
  * (amax computed now, from these values).  layouts is a bitmask of
  * FP8_LAYOUT_ROW / FP8_LAYOUT_COL; both layouts come from one pass over x
- * ("fused cast emits ordinary and transposed layouts", "Native FP8 MLP
- * reconstruction", implementation paragraph).  Requesting a single layout
- * gives bytes identical to those of the fused call.
+ * (the fused dual-layout cast of "Native FP8 MLP reconstruction",
+ * implementation paragraph).  Requesting a single layout gives bytes
+ * identical to those of the fused call.
  * Writes out->q_row / out->q_col (as requested), out->scale, out->scale_inv,
  * and for 1x128 with the col layout out->scale_col / out->scale_inv_col;
  * out->amax if non-NULL and TENSOR.

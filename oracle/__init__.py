@@ -14,10 +14,12 @@ orders them:
   backward  dYq = quant(dY, E5M2) with its own current amax,
             dX = GEMM(dYq_row, Wq_col), dW = GEMM(dYq_col, Xq_col)
 
-("Native FP8 MLP reconstruction", implementation paragraph: current
-tensorwise amax, E4M3 inputs/weights, E5M2 incoming gradients, BF16 outputs,
-fused cast writing ordinary and transposed layouts, forward-rounded X/W reused
-in the backward pass, gradient rounded separately.)  Block scaling follows the
+The recipe is the one of "Native FP8 MLP reconstruction" (implementation
+paragraph): each tensor is scaled by its own amax taken on the current call;
+activations and weights are encoded as E4M3, the incoming gradient as E5M2;
+one cast pass produces both the ordinary and the transposed layout; every GEMM
+writes BF16; the backward pass reuses the X and W codes of the forward pass
+and quantizes the gradient by itself.  Block scaling follows the
 Float8BlockScaling recipe named in TransformerEngine issue 2852 (opening
 post): 1x128 blocks for activations and gradients, 128x128 for weights.
 

@@ -10,7 +10,8 @@
 
 Every quantized byte and scale of X, W and dY is compared with the oracle
 (bit-exact); Y, dX and dW are compared on 4096 sampled outputs each, to the
-BF16 tolerance plus the FP8 matrix-core window bound.  Operands are drawn
+BF16 tolerance plus the FP8 matrix-core window bound, and to the emulation of
+the matrix cores' accumulation (tests/_util.py).  Operands are drawn
 with the seeded device generator (synth.workload_on_device)."""
 import numpy as np
 import pytest
@@ -18,7 +19,7 @@ import torch
 
 import oracle
 import synth
-from _util import check_bf16, mfma_window_bound_rows, to_np_u16, to_np_u8
+from _util import check_gemm_rows, to_np_u16, to_np_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -104,8 +105,7 @@ def test_config_full_size(fp8, name):
             ref = oracle.gemm_block_sampled(A, fa, sA, B, fb, sB, ii, jj)
             t = block_row_factors(gname, q1, q2, ii, jj, N, K, M)
         got = to_np_u16(out)[ii, jj]
-        hw = mfma_window_bound_rows(A[ii], fa, B[jj], fb, t)
-        rep = check_bf16(got, ref, Kc, name + " " + gname, hw)
+        rep = check_gemm_rows(got, ref, A[ii], fa, B[jj], fb, t, Kc, name + " " + gname)
         print(name, gname, rep, flush=True)
 
 

@@ -21,7 +21,7 @@ import torch
 
 import oracle
 import synth
-from _util import check_bf16, mfma_window_bound, to_np_u16, to_np_u8
+from _util import check_gemm, to_np_u16, to_np_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -199,7 +199,7 @@ def test_mlp_block_layers(fp8, recipe):
         t = np.float32(xq["scale_inv"] * ctx2["wq"]["scale_inv"])
     else:
         t = (xq["scale_inv_row"], np.repeat(ctx2["wq"]["scale_inv"], 128, axis=0))
-    check_bf16(to_np_u16(y), yr, h, "Y2", mfma_window_bound(xq["q_row"], "e4m3", ctx2["wq"]["q_row"], "e4m3", t))
+    print(check_gemm(to_np_u16(y), yr, xq["q_row"], "e4m3", ctx2["wq"]["q_row"], "e4m3", t, h, "Y2"), flush=True)
 
     # the first linear's backward, its incoming gradient dGELU(dH, A)
     _, ctx1 = oracle.linear_fwd(synth.bits(x), synth.bits(w1), "tensor" if recipe == "tensor" else "block")
@@ -212,8 +212,8 @@ def test_mlp_block_layers(fp8, recipe):
     else:
         tdx = (dyq["scale_inv_row"], np.repeat(wq["scale_inv"].T, 128, axis=0))
         tdw = (dyq["scale_inv_col"], xq1["scale_inv_col"])
-    check_bf16(to_np_u16(dx), dxr, h, "dX1", mfma_window_bound(dyq["q_row"], "e5m2", wq["q_col"], "e4m3", tdx))
-    check_bf16(to_np_u16(dw1), dw1r, N, "dW1", mfma_window_bound(dyq["q_col"], "e5m2", xq1["q_col"], "e4m3", tdw))
+    print(check_gemm(to_np_u16(dx), dxr, dyq["q_row"], "e5m2", wq["q_col"], "e4m3", tdx, h, "dX1"), flush=True)
+    print(check_gemm(to_np_u16(dw1), dw1r, dyq["q_col"], "e5m2", xq1["q_col"], "e4m3", tdw, N, "dW1"), flush=True)
 
     # the unfused calls give the same bits
     u1, u2 = fp8.Fp8Linear(N, d, h, R), fp8.Fp8Linear(N, h, d, R)

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from _util import check_bf16, mfma_window_bound, to_np_u16, to_np_u8
+from _util import check_gemm, to_np_u16, to_np_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,7 @@ def check_q(q, ref, scaling_kind):
         assert f(q.scale_inv)[0] == np.float32(ref["scale_inv"]).view(np.uint32)
     elif scaling_kind == "1x128":
         assert np.array_equal(f(q.scale), ref["scale_row"].view(np.uint32))
+        assert np.array_equal(f(q.scale_inv), ref["scale_inv_row"].view(np.uint32))
         assert np.array_equal(f(q.scale_col), ref["scale_col"].view(np.uint32))
         assert np.array_equal(f(q.scale_inv_col), ref["scale_inv_col"].view(np.uint32))
     else:
@@ -44,7 +45,7 @@ def check_q(q, ref, scaling_kind):
 
 
 def gemm_operands(ctx, dyq, recipe, N, K, M):
-    """(name, A, fa, B, fb, t, Kc) of the three GEMMs, t as mfma_window_bound
+    """(name, A, fa, B, fb, t, Kc) of the three GEMMs, t as check_gemm
     takes it (scalar, or per-row / per-128-block factors of both operands)."""
     xq, wq = ctx["xq"], ctx["wq"]
     if recipe == "tensor":
@@ -88,7 +89,7 @@ def test_linear_parity(fp8, name, N, K, M, recipe, sig, frac):
     outs = {"Y": (y, yr), "dX": (dx, dxr), "dW": (dw, dwr)}
     for gname, A, fa, B, fb, t, Kc in gemm_operands(ctx, dyq, recipe, N, K, M):
         got, ref = outs[gname]
-        check_bf16(to_np_u16(got), ref, Kc, name + " " + gname, mfma_window_bound(A, fa, B, fb, t))
+        print(check_gemm(to_np_u16(got), ref, A, fa, B, fb, t, Kc, name + " " + gname), flush=True)
 
 
 @pytest.mark.parametrize("recipe", ["tensor", "block"])
@@ -174,8 +175,7 @@ def test_full_size_512x2048_sampled(fp8):
         jj = rng.integers(0, J, n)
         ref = oracle.gemm_tensor_sampled(A, fa, B, fb, sa, sb, ii, jj)
         got = to_np_u16(out)[ii, jj]
-        hw = mfma_window_bound(A, fa, B, fb, np.float32(sa * sb), ii, jj)
-        check_bf16(got, ref, Kc, "full-size " + name, hw)
+        print(check_gemm(got, ref, A, fa, B, fb, np.float32(sa * sb), Kc, "full-size " + name, ii, jj), flush=True)
 
 
 def test_forward_weight_larger_than_input(fp8):
@@ -201,5 +201,6 @@ def test_forward_weight_larger_than_input(fp8):
     ii = rng.integers(0, N, 2048)
     jj = rng.integers(0, M, 2048)
     ref = oracle.gemm_tensor_sampled(xq["q_row"], "e4m3", wq["q_row"], "e4m3", xq["scale_inv"], wq["scale_inv"], ii, jj)
-    hw = mfma_window_bound(xq["q_row"], "e4m3", wq["q_row"], "e4m3", np.float32(xq["scale_inv"] * wq["scale_inv"]), ii, jj)
-    check_bf16(to_np_u16(y)[ii, jj], ref, K, "weight-larger Y", hw)
+    t = np.float32(xq["scale_inv"] * wq["scale_inv"])
+    print(check_gemm(to_np_u16(y)[ii, jj], ref, xq["q_row"], "e4m3", wq["q_row"], "e4m3", t, K, "weight-larger Y", ii, jj),
+          flush=True)
