@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=int, default=131072)
     ap.add_argument("--reps", type=int, default=20, help="instrumented steps in the per-call breakdown")
-    ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=131072, help="token sample of the oracle baseline (all threads)")
+    ap.add_argument("--cpu-tokens-1core", type=int, default=8192, help="token sample of the one-thread oracle leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-stage breakdown")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured ceilings (HBM probes, sustained GEMM clock)")
@@ -322,9 +323,10 @@ def stage_times(fp8, torch, layers, reps, recipe="tensor"):
     act = fp8.SCALE_1x128 if block else fp8.SCALE_TENSOR
     wsc = fp8.SCALE_128x128 if block else fp8.SCALE_TENSOR
     # algorithmic bytes per element: tensorwise = amax read 2 + cast read 2 +
-    # two 1-byte layouts; block = one read + two layouts + fp32 scale and
-    # inverse scale per 128-block of each layout (1x128) or per tile (128x128)
-    act_b, w_b = (4 + 16 / 128, 4 + 8 / 16384) if block else (6, 6)
+    # two 1-byte layouts; block = one read + two layouts + the fp32
+    # dequantisation factor of each block of each layout (1x128: one per 128
+    # elements per layout; 128x128: one per tile, shared by both layouts)
+    act_b, w_b = (4 + 8 / 128, 4 + 4 / 16384) if block else (6, 6)
     seq = []
     for L in layers:
         lin, N, K, M = L["lin"], L["N"], L["K"], L["M"]
@@ -654,23 +656,56 @@ def ceilings(fp8, torch, synth, dev):
     return res
 
 
-def time_steps(torch, layers, steps, warmup):
-    """ms per step (events around `steps` steps after `warmup` untimed ones)."""
+def timing_groups(torch, step, steps, warmup, groups=5):
+    """The timing protocol: `warmup` untimed steps, then exactly `steps` steps
+    split into `groups` consecutive groups (as equal as possible), an event
+    pair around each group on torch's current stream (the stream the library
+    launches on), a device synchronisation on both sides of the timed region.
+    Returns the median group's ms per step, the mean over all steps and the
+    per-group figures (the pages report medians of five timing groups)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    g = max(1, min(groups, steps))
+    sizes = [steps // g + (1 if i < steps % g else 0) for i in range(g)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in sizes]
+    for (e0, e1), n in zip(ev, sizes):
+        e0.record()
+        for _ in range(n):
+            step()
+        e1.record()
+    torch.cuda.synchronize()
+    per = [e0.elapsed_time(e1) / n for (e0, e1), n in zip(ev, sizes)]
+    total = sum(e0.elapsed_time(e1) for e0, e1 in ev)
+    med = sorted(per)[len(per) // 2] if len(per) % 2 else sum(sorted(per)[len(per) // 2 - 1:len(per) // 2 + 1]) / 2
+    return {"ms": med, "mean_ms": total / steps, "group_steps": sizes, "group_ms": per}
+
+
+def linear_step(layers):
     def step():
         for L in layers:
             L["lin"].forward(L["x"], L["w"], y=L["y"])
             L["lin"].backward(L["dy"], dx=L["dx"], dw=L["dw"])
+    return step
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+
+def time_steps(torch, layers, steps, warmup):
+    """ms per step (median of five timing groups over `steps` steps after
+    `warmup` untimed ones)."""
+    return timing_groups(torch, linear_step(layers), steps, warmup)["ms"]
+
+
+def latency_small(fp8, torch, synth, dev, steps=500, warmup=50):
+    """The small linear 512 -> 512 at N = 1024 (tensorwise, X ~ N(0,1),
+    W ~ N(0,0.02), dY ~ N(0,1e-3), seed 0): forward + backward latency in
+    microseconds, median of five timing groups."""
+    layers, _ = workload_layers(fp8, torch, synth, "linear_512x512_n1024", dev)
+    L = layers[0]
+    t = timing_groups(torch, linear_step(layers), steps, warmup)
+    return {"workload": "fp8 linear 512->512 fwd+bwd, N=1024, tensorwise current scaling",
+            "us_per_step": round(t["ms"] * 1e3, 2), "us_per_step_mean": round(t["mean_ms"] * 1e3, 2),
+            "steps": steps, "value": round(6 * L["N"] * L["K"] * L["M"] / (t["ms"] / 1e3) / 1e12, 2),
+            "unit": "TFLOP/s"}
 
 
 def chain_times(fp8, torch, synth, N, steps, warmup, dev):
@@ -881,24 +916,90 @@ def roofline_of(stage):
     return r
 
 
-def cpu_baseline(shapes, tokens):
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_step(oracle, xb, wb, dyb, stage_s):
+    """The oracle's linear forward + backward (tensorwise), the same calls
+    oracle.linear_fwd / linear_bwd make, timed per stage."""
+    def timed(name, fn, *a):
+        t0 = time.perf_counter()
+        r = fn(*a)
+        stage_s[name] = stage_s.get(name, 0.0) + time.perf_counter() - t0
+        return r
+    N, K = xb.shape
+    M = wb.shape[0]
+    xq = timed("quantize_x", oracle.quant_tensor, xb, "e4m3")
+    wq = timed("quantize_w", oracle.quant_tensor, wb, "e4m3")
+    a, sa, b, sb = oracle.fprop_operands(xq, wq, "tensor", N, K, M)
+    timed("gemm_fprop", oracle.gemm_tensor, a, "e4m3", b, "e4m3", sa.s[0], sb.s[0])
+    dyq = timed("quantize_dy", oracle.quant_tensor, dyb, "e5m2")
+    a, sa, b, sb = oracle.dgrad_operands(dyq, wq, "tensor", N, K, M)
+    timed("gemm_dgrad", oracle.gemm_tensor, a, "e5m2", b, "e4m3", sa.s[0], sb.s[0])
+    a, sa, b, sb = oracle.wgrad_operands(dyq, xq, "tensor", N, K, M)
+    timed("gemm_wgrad", oracle.gemm_tensor, a, "e5m2", b, "e4m3", sa.s[0], sb.s[0])
+
+
+def cpu_baseline(shapes, tokens, tokens_1core):
     """The oracle as it stands (plain C, OpenMP) on a token sample of the same
-    two linears, forward + backward, on this host's cores."""
+    two linears, forward + backward, on this host: once on all its threads
+    (N = `tokens`), once on one thread (N = `tokens_1core`), each timed per
+    stage (quantize of X, W, dY; the three GEMMs)."""
     import oracle
     import synth
-    t_total = 0.0
-    flops = 0
-    for idx, (K, M) in enumerate(shapes):
-        x, w, dy = synth.operands(tokens, K, M, seed=100 + idx)
-        xb, wb, dyb = synth.bits(x), synth.bits(w), synth.bits(dy)
-        t0 = time.perf_counter()
-        _, ctx = oracle.linear_fwd(xb, wb, "tensor")
-        oracle.linear_bwd(dyb, ctx)
-        t_total += time.perf_counter() - t0
-        flops += 6 * tokens * K * M
-    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "fwd+bwd of 512->2048 and 2048->512 at N=%d tokens (of 131072), %.1f s" % (tokens, t_total)}
+    legs = {}
+    all_threads = oracle.num_threads()
+    for leg, n_tok, threads in (("all_cores", tokens, all_threads), ("one_core", tokens_1core, 1)):
+        oracle.set_num_threads(threads)
+        stage_s = {}
+        flops = 0
+        for idx, (K, M) in enumerate(shapes):
+            x, w, dy = synth.operands(n_tok, K, M, seed=100 + idx)
+            _oracle_step(oracle, synth.bits(x), synth.bits(w), synth.bits(dy), stage_s)
+            flops += 6 * n_tok * K * M
+        t = sum(stage_s.values())
+        legs[leg] = {"tokens": n_tok, "threads": threads, "s": round(t, 3),
+                     "value": round(flops / t / 1e12, 6), "unit": "TFLOP/s",
+                     "stage_s": {k: round(v, 3) for k, v in stage_s.items()}}
+    oracle.set_num_threads(all_threads)
+    a = legs["all_cores"]
+    return {"value": a["value"], "unit": "TFLOP/s", "cores": all_threads, "kind": "oracle",
+            "cpu_model": _cpu_model(), "one_core": legs["one_core"], "all_cores": legs["all_cores"],
+            "sample": "fwd+bwd of 512->2048 and 2048->512 at N=%d tokens (of 131072) on %d threads, %.1f s; "
+                      "and at N=%d on 1 thread, %.1f s" % (tokens, all_threads, a["s"], tokens_1core,
+                                                           legs["one_core"]["s"])}
+
+
+def targets(stages, configs):
+    """The goals next to what this run measured: >= 80% of the HBM peak on
+    the quantize kernels, >= 70% of the dense FP8 matrix-core peak on the
+    large GEMMs (the 8192 x 8192 weight at N = 16384, and the gradient GEMMs
+    of 512 -> 8192 at N = 262144)."""
+    q = [s["gbs"] / HBM_PEAK_GBS for s in stages if s["stage"].startswith("quant_x") or
+         s["stage"].startswith("quant_dy")]
+    out = {"quantize_hbm_frac": {"target": 0.80, "measured_min": round(min(q), 3), "measured_max": round(max(q), 3),
+                                 "over": "activation and gradient quantizes of the headline step"}}
+    if configs:
+        fr = []
+        for name in ("linear_8192x8192_n16384", "linear_8192x8192_n16384_block"):
+            if name in configs:
+                fr += [v["mfma_frac"] for v in configs[name]["gemms"].values()]
+        for name in ("linear_512x8192_n262144", "linear_512x8192_n262144_block"):
+            if name in configs:
+                fr += [v["mfma_frac"] for k, v in configs[name]["gemms"].items() if k in ("dgrad", "wgrad")]
+        if fr:
+            out["large_gemm_mfma_frac"] = {"target": 0.70, "measured_min": round(min(fr), 3),
+                                           "measured_max": round(max(fr), 3),
+                                           "over": "GEMMs of the 8192x8192 weight at N=16384 and gradient GEMMs of "
+                                                   "512->8192 at N=262144, both recipes"}
+    return out
 
 
 def main():
@@ -927,11 +1028,13 @@ def main():
     shapes = SHAPES
     layers = make_layers(fp8, torch, synth, N, "tensor", dev)
     t0 = time.perf_counter()
-    ms = time_steps(torch, layers, args.steps, args.warmup)
+    timing = timing_groups(torch, linear_step(layers), args.steps, args.warmup)
     wall = time.perf_counter() - t0
+    ms = timing["ms"]
     flops = sum(6 * N * K * M for K, M in shapes)
     value = flops / (ms / 1e3) / 1e12
-    print("timed %d steps: %.4f ms/step (wall %.3f s)" % (args.steps, ms, wall), file=sys.stderr, flush=True)
+    print("timed %d steps in %d groups: median group %.4f ms/step, mean %.4f ms/step (wall %.3f s)" %
+          (args.steps, len(timing["group_steps"]), ms, timing["mean_ms"], wall), file=sys.stderr, flush=True)
 
     if args.copy_reference:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float16, device=dev)
@@ -951,6 +1054,8 @@ def main():
     q = [s for s in stages if s["stage"].startswith("quant")]
     quant_gbs = sum(s["bytes"] for s in q) / sum(s["ms"] for s in q) / 1e6
     dom = max(stages, key=lambda s: s["ms"])     # the stage (one library call) that takes longest
+    lat = latency_small(fp8, torch, synth, dev)
+    print("512->512 at N=1024: %.2f us/step" % lat["us_per_step"], file=sys.stderr, flush=True)
     block = None
     if not args.no_block:
         # the same two linears under block scaling (X, dY 1x128; W 128x128)
@@ -1019,6 +1124,10 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "timing": {"protocol": "median of %d timing groups of %s steps (events on the launch stream)" %
+                   (len(timing["group_steps"]), "/".join(str(n) for n in timing["group_steps"])),
+                   "ms_per_step_mean": round(timing["mean_ms"], 4),
+                   "group_ms_per_step": [round(v, 4) for v in timing["group_ms"]]},
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": round(value / pages_tflops, 3) if N == 131072 else None,
         "baseline_note": "pages' RTX 4090 fused-layout FP8 medians (5.4075 + 5.4264 ms = %.1f TFLOP/s): context" % pages_tflops,
@@ -1030,6 +1139,8 @@ def main():
         "stages": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()} for s in stages],
         "roofline": roofline_of(dom),
         "cpu_baseline": None,
+        "latency_512x512_n1024": lat,
+        "targets": targets(stages, configs),
         "block_scaling": block,
         "amax_handoff": chain,
         "bf16_comparator": bf16,
@@ -1040,7 +1151,7 @@ def main():
         "ceilings": ceil,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(shapes, args.cpu_tokens, args.cpu_tokens_1core)
     print(json.dumps(out), flush=True)
 
 
