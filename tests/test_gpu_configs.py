@@ -3,10 +3,7 @@
 - block scaling 512 -> 8192 at N = 131072 with 1% outliers (x100);
 - the square 8192 x 8192 weight at N = 16384 and 512 -> 8192 at N = 262144,
   tensorwise and block-scaled;
-- the 8-layer MLP stack (16 linears, d = 512 -> 2048 -> 512, GELU between) at
-  131072 tokens per microbatch with gradient accumulation over 4
-  microbatches: weight cache (quantize on microbatch 1, reuse on 2-4) against
-  requantizing every microbatch, bitwise.
+(the 8-block MLP stack with the weight cache is in test_gpu_mlp_stack.py).
 
 Every quantized byte and scale of X, W and dY is compared with the oracle
 (bit-exact); Y, dX and dW are compared on 4096 sampled outputs each, to the
@@ -107,71 +104,3 @@ def test_config_full_size(fp8, name):
         got = to_np_u16(out)[ii, jj]
         rep = check_gemm_rows(got, ref, A[ii], fa, B[jj], fb, t, Kc, name + " " + gname)
         print(name, gname, rep, flush=True)
-
-
-def _gelu(a):
-    x = a.float()
-    return (0.5 * x * (1.0 + torch.erf(x * 0.7071067811865476))).to(torch.bfloat16)
-
-
-def _dgelu(a, g):
-    x = a.float()
-    cdf = 0.5 * (1.0 + torch.erf(x * 0.7071067811865476))
-    pdf = torch.exp(-0.5 * x * x) * 0.3989422804014327
-    return (g.float() * (cdf + x * pdf)).to(torch.bfloat16)
-
-
-def _run_stack(fp8, lins, weights, xs, dys, cached):
-    """Forward + backward of the stack over the microbatches (linear 2p is
-    the up projection, 2p+1 the down projection, GELU between); returns the
-    outputs, the input gradients and the fp32-accumulated dW of each linear."""
-    pairs = len(lins) // 2
-    acc = [torch.zeros(w.shape, dtype=torch.float32, device="cuda") for w in weights]
-    outs, dxs = [], []
-    for mb, (x, dy) in enumerate(zip(xs, dys)):
-        flag = (mb == 0) if cached else None
-        wsel = (lambda l: weights[l] if (not cached or mb == 0) else None)
-        h, pre = x, []
-        for p in range(pairs):
-            a = lins[2 * p].forward(h, wsel(2 * p), is_first_microbatch=flag)
-            pre.append(a)
-            h = lins[2 * p + 1].forward(_gelu(a), wsel(2 * p + 1), is_first_microbatch=flag)
-        outs.append(h.clone())
-        dh = dy
-        for p in reversed(range(pairs)):
-            dg, dw_down = lins[2 * p + 1].backward(dh)
-            acc[2 * p + 1] += dw_down.float()
-            dh, dw_up = lins[2 * p].backward(_dgelu(pre[p], dg))
-            acc[2 * p] += dw_up.float()
-        dxs.append(dh.clone())
-    torch.cuda.synchronize()
-    return outs, dxs, acc
-
-
-def test_mlp_stack_weight_cache_bitwise(fp8):
-    N, d, h, layers, mbs = 131072, 512, 2048, 8, 4
-    print("mlp stack", N, d, h, layers, mbs, flush=True)
-    g = torch.Generator(device="cuda")
-    g.manual_seed(4)
-    weights = []
-    for _ in range(layers):
-        weights.append(synth.normal_bf16((h, d), 0.02, g, device="cuda"))
-        weights.append(synth.normal_bf16((d, h), 0.02, g, device="cuda"))
-    xs = [synth.normal_bf16((N, d), 1.0, g, device="cuda") for _ in range(mbs)]
-    dys = [synth.normal_bf16((N, d), 1e-3, g, device="cuda") for _ in range(mbs)]
-    shapes = [(d, h), (h, d)] * layers      # (K, M) of each linear
-    res = {}
-    for cached in (True, False):
-        lins = [fp8.Fp8Linear(N, K, M, fp8.RECIPE_TENSOR, cache=cached) for K, M in shapes]
-        res[cached] = _run_stack(fp8, lins, weights, xs, dys, cached)
-        if cached:
-            assert all(l.cache.fills == 1 and l.cache.valid for l in lins)
-        del lins
-        torch.cuda.empty_cache()
-    (o1, x1, a1), (o2, x2, a2) = res[True], res[False]
-    for mb in range(mbs):
-        assert torch.equal(o1[mb], o2[mb]), ("output", mb)
-        assert torch.equal(x1[mb], x2[mb]), ("input gradient", mb)
-    for l in range(2 * layers):
-        assert torch.equal(a1[l], a2[l]), ("dW", l)
-        assert torch.isfinite(a1[l]).all()

@@ -148,12 +148,15 @@ def test_linear_deterministic(fp8):
         assert torch.equal(a, b)
 
 
-def test_full_size_512x2048_sampled(fp8):
-    """The 512 -> 2048 linear at N = 131072 in the bench's launch
-    configuration: every quantized byte and scale of X, W and dY bit-exact;
-    4096 sampled outputs each of Y, dX and dW against the oracle."""
-    N, K, M = 131072, 512, 2048
-    d = synth.workload("linear_512x2048_n131072")
+@pytest.mark.parametrize("workload", ["linear_512x2048_n131072", "linear_2048x512_n131072"])
+def test_full_size_sampled(fp8, workload):
+    """The two linears of the headline step (512 -> 2048 and 2048 -> 512 at
+    N = 131072) in the bench's launch configuration: every quantized byte and
+    scale of X, W and dY bit-exact; 4096 sampled outputs each of Y, dX and dW
+    against the oracle and the matrix-core emulation."""
+    print("full size", workload, flush=True)
+    d = synth.workload(workload)
+    N, K, M = d["N"], d["K"], d["M"]
     lin = fp8.Fp8Linear(N, K, M, fp8.RECIPE_TENSOR)
     y = lin.forward(cuda_bf16(d["x"]), cuda_bf16(d["w"]))
     dx, dw = lin.backward(cuda_bf16(d["dy"]))
