@@ -333,6 +333,18 @@ class Fp8Linear:
         self._last_flag = flag
         return y
 
+    def forward_noalloc(self, x, w, y, is_first_microbatch=None, stream=None, x_amax=None, y_amax=None):
+        """forward() through fp8_linear_fwd_noalloc: the library's per-device
+        scratch instead of this layer's workspace; y must be given (nothing
+        is allocated here either)."""
+        flag = -1 if is_first_microbatch is None else int(bool(is_first_microbatch))
+        cache = self.cache.handle if (self.cache is not None and flag != -1) else None
+        _lib.check(lib().fp8_linear_fwd_noalloc(_ptr(x), _ptr(w), self.N, self.K, self.M, self.recipe, cache, flag,
+                                                _ptr(y), ctypes.byref(self._sx), ctypes.byref(self._wq),
+                                                _ptr(x_amax), _ptr(y_amax), _stream(stream)))
+        self._last_flag = flag
+        return y
+
     def backward(self, dy, dx=None, dw=None, need_dx=True, need_dw=True, stream=None, dy_amax=None,
                  dx_amax=None, gelu_input=None):
         """dy_amax: dY's amax partials from its producer (skips dY's amax

@@ -19,6 +19,7 @@ LAYOUT_ROW, LAYOUT_COL = 1, 2
 STATUS = {0: "FP8_OK", 1: "FP8_ERR_NULL", 2: "FP8_ERR_SHAPE", 3: "FP8_ERR_ALIGN", 4: "FP8_ERR_ENUM",
           5: "FP8_ERR_WORKSPACE", 6: "FP8_ERR_CACHE_EMPTY", 7: "FP8_ERR_CACHE_MISMATCH", 8: "FP8_ERR_HIP",
           9: "FP8_ERR_UNIMPLEMENTED"}
+NOALLOC_SCRATCH_BYTES = 8 << 20   # FP8_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/fp8_linear.h declares
 EXPORTS = [
@@ -28,7 +29,7 @@ EXPORTS = [
     "fp8_wcache_create", "fp8_wcache_invalidate", "fp8_wcache_valid", "fp8_wcache_fills",
     "fp8_wcache_destroy", "fp8_linear_workspace_bytes", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_gelu", "fp8_dgelu", "fp8_quantize_gelu", "fp8_quantize_dgelu", "fp8_linear_fwd_gelu",
-    "fp8_linear_bwd_dgelu",
+    "fp8_linear_bwd_dgelu", "fp8_linear_fwd_noalloc",
     "fp8_status_string", "fp8_last_error", "fp8_version",
 ]
 
@@ -87,6 +88,7 @@ def load():
         "fp8_quantize_dgelu": (I, [P, P, I64, I64, I, I, U, QP, P, SZ, P]),
         "fp8_linear_fwd_gelu": (I, [P, P, I64, I64, I64, I, P, I, P, QP, QP, P, P, SZ, P]),
         "fp8_linear_bwd_dgelu": (I, [P, P, I64, I64, I64, I, QP, P, QP, QP, P, P, P, P, SZ, P]),
+        "fp8_linear_fwd_noalloc": (I, [P, P, I64, I64, I64, I, P, I, P, QP, QP, P, P, P]),
         "fp8_status_string": (ctypes.c_char_p, [I]),
         "fp8_last_error": (ctypes.c_char_p, []),
         "fp8_version": (ctypes.c_char_p, []),

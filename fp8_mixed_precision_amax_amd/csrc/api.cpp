@@ -415,14 +415,29 @@ size_t fp8_linear_workspace_bytes(int64_t N, int64_t K, int64_t M, fp8_recipe re
     return kPartialBytes + (g > kPartialBytes ? g : kPartialBytes);
 }
 
-static fp8_status check_linear_common(int64_t N, int64_t K, int64_t M, int recipe, void* ws, size_t ws_bytes) {
+static fp8_status check_linear_dims(int64_t N, int64_t K, int64_t M, int recipe) {
     FP8_TRY(check_dims("linear N x K", N, K));
     FP8_TRY(check_dims("linear M", M, 128));
     // N, K and M are each the contraction of one of the three GEMMs
     if (N >= kMaxContraction || K >= kMaxContraction || M >= kMaxContraction)
         return fail(FP8_ERR_SHAPE, "linear dimensions must be below 2^23");
     if (recipe != FP8_RECIPE_TENSOR && recipe != FP8_RECIPE_BLOCK) return fail(FP8_ERR_ENUM, "unknown recipe %d", recipe);
-    const size_t need = fp8_linear_workspace_bytes(N, K, M, static_cast<fp8_recipe>(recipe));
+    return FP8_OK;
+}
+
+// Workspace of the forward pass alone: the input's amax partials, then the
+// forward GEMM's split-K partials (at least 4 KiB, where the tensorwise
+// forward keeps the weight's amax partials).
+static size_t linear_fwd_ws_bytes(int64_t N, int64_t K, int64_t M) {
+    const size_t g = fp8k::gemm_ws_bytes(N, M, K);
+    return kPartialBytes + (g > kPartialBytes ? g : kPartialBytes);
+}
+
+// need == 0: the whole linear's workspace (fp8_linear_workspace_bytes)
+static fp8_status check_linear_common(int64_t N, int64_t K, int64_t M, int recipe, void* ws, size_t ws_bytes,
+                                      size_t need = 0) {
+    FP8_TRY(check_linear_dims(N, K, M, recipe));
+    if (!need) need = fp8_linear_workspace_bytes(N, K, M, static_cast<fp8_recipe>(recipe));
     if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     FP8_TRY(check_ptr16("ws", ws));
     return FP8_OK;
@@ -448,11 +463,12 @@ static fp8_status check_amax_handoff(int recipe, const void* in, const void* out
 
 // act 1: the linear's input is GELU(x) (x the pre-activation), quantized
 // without being written out
+// ws_need: 0 for the whole linear's workspace, else the forward's alone
 static fp8_status linear_fwd(const void* x, int act, const void* w, int64_t N, int64_t K, int64_t M,
                              fp8_recipe recipe, fp8_wcache cache, int flag, void* y, const fp8_qtensor* saved_x,
                              const fp8_qtensor* w_q, const void* x_amax_partials, void* y_amax_partials, void* ws,
-                             size_t ws_bytes, void* stream) {
-    FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes));
+                             size_t ws_bytes, void* stream, size_t ws_need = 0) {
+    FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes, ws_need));
     if (flag != -1 && flag != 0 && flag != 1) return fail(FP8_ERR_ENUM, "is_first_microbatch must be -1, 0 or 1");
     FP8_TRY(check_ptr16("x", x));
     FP8_TRY(check_ptr16("y", y));
@@ -506,6 +522,23 @@ fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, in
                           void* stream) {
     return linear_fwd(x, 0, w, N, K, M, recipe, cache, flag, y, saved_x, w_q, x_amax_partials, y_amax_partials, ws,
                       ws_bytes, stream);
+}
+
+fp8_status fp8_linear_fwd_noalloc(const void* x, const void* w, int64_t N, int64_t K, int64_t M,
+                                  fp8_recipe recipe, fp8_wcache cache, int flag, void* y,
+                                  const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
+                                  const void* x_amax_partials, void* y_amax_partials, void* stream) {
+    FP8_TRY(check_linear_dims(N, K, M, recipe));
+    const size_t need = linear_fwd_ws_bytes(N, K, M);
+    if (need > fp8k::kNoallocScratchBytes)
+        return fail(FP8_ERR_WORKSPACE,
+                    "this forward needs %zu bytes of scratch (split-K partials of its GEMM), more than the %zu-byte "
+                    "device scratch of fp8_linear_fwd_noalloc; use fp8_linear_fwd with a workspace",
+                    need, fp8k::kNoallocScratchBytes);
+    void* scratch = nullptr;
+    FP8_TRY(hip_status(fp8k::noalloc_scratch(&scratch), "device scratch address"));
+    return linear_fwd(x, 0, w, N, K, M, recipe, cache, flag, y, saved_x, w_q, x_amax_partials, y_amax_partials,
+                      scratch, fp8k::kNoallocScratchBytes, stream, need);
 }
 
 fp8_status fp8_linear_fwd_gelu(const void* x_pre, const void* w, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,

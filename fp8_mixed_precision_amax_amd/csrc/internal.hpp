@@ -85,4 +85,10 @@ hipError_t launch_gemm_block_wide(const GemmLaunch& l, int splits, hipStream_t s
 size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
 
+// Scratch of the entry point that allocates nothing (noalloc.hip): a device
+// array of kNoallocScratchBytes per GPU; *out receives the current device's
+// address of it (taken once per device).
+constexpr size_t kNoallocScratchBytes = size_t(8) << 20;
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace fp8k

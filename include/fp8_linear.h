@@ -306,6 +306,35 @@ fp8_status fp8_linear_bwd(const void* dy_bf16, int64_t N, int64_t K, int64_t M, 
                           const void* dy_amax_partials, void* dx_amax_partials,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------- forward without any allocation ------------------ */
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * forward pass exactly as fp8_linear_fwd (same kernels, bitwise the same
+ * Y, saved_x and quantized weight), with no workspace argument.  Its scratch
+ * (the amax partials of X and W, and the forward GEMM's split-K partials) is
+ * a device array of FP8_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends; nothing is allocated, and nothing
+ * in it needs clearing (every call writes what it reads).
+ *  - A shape whose forward needs more scratch than that (a short output
+ *    whose GEMM would split a long contraction into large partial sums)
+ *    gives FP8_ERR_WORKSPACE before anything is enqueued; fp8_linear_fwd
+ *    with a workspace serves it.
+ *  - All calls on one GPU share that GPU's array: calls that may overlap on
+ *    one GPU (different streams, different threads) race and give undefined
+ *    results; order them (one stream, or events).
+ *  - The first call on a device looks up that device's copy of the array
+ *    (hipGetSymbolAddress); a failure there gives FP8_ERR_HIP.
+ * Arguments as fp8_linear_fwd without (ws, ws_bytes).
+ */
+#define FP8_NOALLOC_SCRATCH_BYTES (8u << 20)
+fp8_status fp8_linear_fwd_noalloc(const void* x_bf16, const void* w_bf16,
+                                  int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
+                                  fp8_wcache cache, int is_first_microbatch,
+                                  void* y_bf16, const fp8_qtensor* saved_x, const fp8_qtensor* w_q,
+                                  const void* x_amax_partials, void* y_amax_partials, void* stream);
+
 /* ----------------------- GELU in an MLP block ------------------------ */
 
 /*

@@ -240,3 +240,22 @@ def test_ceilings_library_exports():
     C.fp8c_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                             ctypes.c_void_p]
     assert C.fp8c_mfma(1, 100, 1, None, None, None) != 0
+
+
+def test_noalloc_forward_rejections(L):
+    """fp8_linear_fwd_noalloc validates shape and recipe, and refuses a
+    forward whose scratch would exceed the fixed device array, before it
+    touches any device: a short output over a long contraction (256 x 8192
+    tokens-by-weight with K = 8192 splits its GEMM 8 ways: 64 MiB of
+    partial sums, above 8 MiB)."""
+    assert _lib.NOALLOC_SCRATCH_BYTES == 8 << 20
+    x = qt()
+    w = qt()
+
+    def call(N, K, M, recipe=0):
+        return L.fp8_linear_fwd_noalloc(A, A, N, K, M, recipe, None, -1, A, ctypes.byref(x), ctypes.byref(w),
+                                        None, None, None)
+    assert call(100, 512, 512) == SHAPE
+    assert call(256, 512, 512, recipe=5) == ENUM
+    assert call(256, 8192, 8192) == WORKSPACE
+    assert b"8388608-byte device scratch" in L.fp8_last_error()
