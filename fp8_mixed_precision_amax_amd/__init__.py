@@ -86,12 +86,19 @@ class QTensor:
                                 self.scale_col, self.scale_inv_col, self.amax)))
 
 
-AMAX_PARTIALS_BYTES = 4096   # FP8_AMAX_PARTIALS_BYTES
+AMAX_PARTIALS_BYTES = 4096         # FP8_AMAX_PARTIALS_BYTES
+GELU_AMAX_PARTIALS_BYTES = 16384   # FP8_GELU_AMAX_PARTIALS_BYTES
 
 
 def amax_partials(device):
     """Device buffer for the amax hand-off (2048 16-bit partial maxima)."""
     return torch.empty(AMAX_PARTIALS_BYTES, dtype=torch.uint8, device=device)
+
+
+def gelu_amax_partials(device):
+    """Device buffer for the GELU amax hand-off (four arrays of 2048 16-bit
+    keys, see fp8_linear.h)."""
+    return torch.empty(GELU_AMAX_PARTIALS_BYTES, dtype=torch.uint8, device=device)
 
 
 def quantize(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None,
@@ -202,10 +209,28 @@ def _act_quantize_on(name, fn, xs, fmt, scaling, layouts, out, stream):
     return out
 
 
-def quantize_gelu(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None):
+def quantize_gelu(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None,
+                  gelu_amax_partials=None):
     """Quantize GELU(x) without writing the activation (fp8_quantize_gelu);
-    tensorwise or 1x128 scaling."""
-    return _act_quantize("quantize_gelu", lib().fp8_quantize_gelu, (x,), fmt, scaling, layouts, out, stream)
+    tensorwise or 1x128 scaling.  gelu_amax_partials (tensorwise only): the
+    GELU amax keys x's producer wrote (fp8_quantize_gelu_from_amax: the
+    cast pass alone)."""
+    if gelu_amax_partials is None:
+        return _act_quantize("quantize_gelu", lib().fp8_quantize_gelu, (x,), fmt, scaling, layouts, out, stream)
+    if scaling != SCALE_TENSOR:
+        raise ValueError("GELU amax partials serve the tensorwise quantize")
+    L = lib()
+    _bf16_pair("quantize_gelu", x)
+    R, C = x.shape
+    with _on(stream):
+        if out is None:
+            out = QTensor(R, C, scaling, _dev(x), row=bool(layouts & LAYOUT_ROW), col=bool(layouts & LAYOUT_COL))
+        wsb = L.fp8_quantize_workspace_bytes(R, C, SCALE_TENSOR)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
+        oc = out.c()
+        _lib.check(L.fp8_quantize_gelu_from_amax(_ptr(x), R, C, fmt, layouts, ctypes.byref(oc),
+                                                 _ptr(gelu_amax_partials), _ptr(ws), wsb, _stream(stream)))
+    return out
 
 
 def quantize_dgelu(dy, x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL, out=None, stream=None):
@@ -228,15 +253,17 @@ def block_gemm_scale(sinv, group):
     return gemm_scale(sinv, group, sinv.stride(0), sinv.stride(1))
 
 
-def gemm(a, fa, sa, b, fb, sb, out=None, stream=None, amax_out=None):
+def gemm(a, fa, sa, b, fb, sb, out=None, stream=None, amax_out=None, gelu_amax_out=None):
     """C[i][j] = bf16(sum_k A[i][k] B[j][k] * scales); a [I, K], b [J, K]
     uint8 FP8 codes; sa / sb are GemmScaleC (see gemm_scale).  amax_out
-    (tensorwise only): receives C's amax partials (fp8_gemm_amax)."""
+    (tensorwise only): receives C's amax partials (fp8_gemm_amax);
+    gelu_amax_out (tensorwise E4M3 x E4M3): receives C's GELU amax partials
+    (fp8_gemm_gelu_amax)."""
     with _on(stream):
-        return _gemm(a, fa, sa, b, fb, sb, out, stream, amax_out)
+        return _gemm(a, fa, sa, b, fb, sb, out, stream, amax_out, gelu_amax_out)
 
 
-def _gemm(a, fa, sa, b, fb, sb, out, stream, amax_out):
+def _gemm(a, fa, sa, b, fb, sb, out, stream, amax_out, gelu_amax_out=None):
     L = lib()
     I, K = a.shape
     J, K2 = b.shape
@@ -246,7 +273,12 @@ def _gemm(a, fa, sa, b, fb, sb, out, stream, amax_out):
         out = torch.empty((I, J), dtype=torch.bfloat16, device=a.device)
     wsb = L.fp8_gemm_workspace_bytes(I, J, K)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=a.device)
-    if amax_out is not None:
+    if gelu_amax_out is not None:
+        if amax_out is not None:
+            raise ValueError("one hand-off per GEMM")
+        _lib.check(L.fp8_gemm_gelu_amax(_ptr(a), fa, sa, _ptr(b), fb, sb, I, J, K, _ptr(out), _ptr(gelu_amax_out),
+                                        _ptr(ws), wsb, _stream(stream)))
+    elif amax_out is not None:
         _lib.check(L.fp8_gemm_amax(_ptr(a), fa, sa, _ptr(b), fb, sb, I, J, K, _ptr(out), _ptr(amax_out), _ptr(ws),
                                    wsb, _stream(stream)))
     else:
@@ -379,3 +411,43 @@ class Fp8Linear:
         """The quantized weight the last forward used (cache or w_q)."""
         use_cache = self.cache is not None and getattr(self, "_last_flag", -1) != -1
         return self.cache.q if use_cache else self.w_q
+
+
+class Fp8Mlp:
+    """The MLP block X [N, D] -> A = X W1^T [N, H] -> Y = GELU(A) W2^T [N, D]
+    in FP8: forward in one library call (fp8_mlp_fwd: the up projection hands
+    the GELU amax keys of A to the down projection's input quantize),
+    backward through the two linears' entry points (the up projection's
+    gradient quantize applies GELU')."""
+
+    def __init__(self, N, D, H, recipe=RECIPE_TENSOR, device="cuda", cache=False):
+        self.N, self.D, self.H, self.recipe = N, D, H, recipe
+        self.up = Fp8Linear(N, D, H, recipe, device, cache)
+        self.down = Fp8Linear(N, H, D, recipe, device, cache)
+        n = lib().fp8_mlp_workspace_bytes(N, D, H, recipe)
+        self.ws, self.ws_bytes = torch.empty(max(n, 16), dtype=torch.uint8, device=device), n
+        self.a = None
+
+    def forward(self, x, w1, w2, y=None, a=None, is_first_microbatch=None, stream=None, x_amax=None, y_amax=None):
+        flag = -1 if is_first_microbatch is None else int(bool(is_first_microbatch))
+        with _on(stream):
+            if a is None:
+                a = torch.empty((self.N, self.H), dtype=torch.bfloat16, device=x.device)
+            if y is None:
+                y = torch.empty((self.N, self.D), dtype=torch.bfloat16, device=x.device)
+        use_cache = self.up.cache is not None and flag != -1
+        c1 = self.up.cache.handle if use_cache else None
+        c2 = self.down.cache.handle if use_cache else None
+        _lib.check(lib().fp8_mlp_fwd(_ptr(x), _ptr(w1), _ptr(w2), self.N, self.D, self.H, self.recipe, c1, c2, flag,
+                                     _ptr(a), _ptr(y), ctypes.byref(self.up._sx), ctypes.byref(self.up._wq),
+                                     ctypes.byref(self.down._sx), ctypes.byref(self.down._wq), _ptr(x_amax),
+                                     _ptr(y_amax), _ptr(self.ws), self.ws_bytes, _stream(stream)))
+        self.up._last_flag = self.down._last_flag = flag
+        self.a = a
+        return y
+
+    def backward(self, dy, stream=None):
+        """(dX, dW1, dW2) of the last forward."""
+        dh, dw2 = self.down.backward(dy, stream=stream)
+        dx, dw1 = self.up.backward(dh, stream=stream, gelu_input=self.a)
+        return dx, dw1, dw2

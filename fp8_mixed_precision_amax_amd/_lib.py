@@ -29,7 +29,8 @@ EXPORTS = [
     "fp8_wcache_create", "fp8_wcache_invalidate", "fp8_wcache_valid", "fp8_wcache_fills",
     "fp8_wcache_destroy", "fp8_linear_workspace_bytes", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_gelu", "fp8_dgelu", "fp8_quantize_gelu", "fp8_quantize_dgelu", "fp8_linear_fwd_gelu",
-    "fp8_linear_bwd_dgelu", "fp8_linear_fwd_noalloc",
+    "fp8_linear_bwd_dgelu", "fp8_linear_fwd_noalloc", "fp8_gemm_gelu_amax", "fp8_quantize_gelu_from_amax",
+    "fp8_mlp_workspace_bytes", "fp8_mlp_fwd",
     "fp8_status_string", "fp8_last_error", "fp8_version",
 ]
 
@@ -89,6 +90,10 @@ def load():
         "fp8_linear_fwd_gelu": (I, [P, P, I64, I64, I64, I, P, I, P, QP, QP, P, P, SZ, P]),
         "fp8_linear_bwd_dgelu": (I, [P, P, I64, I64, I64, I, QP, P, QP, QP, P, P, P, P, SZ, P]),
         "fp8_linear_fwd_noalloc": (I, [P, P, I64, I64, I64, I, P, I, P, QP, QP, P, P, P]),
+        "fp8_gemm_gelu_amax": (I, [P, I, GemmScaleC, P, I, GemmScaleC, I64, I64, I64, P, P, P, SZ, P]),
+        "fp8_quantize_gelu_from_amax": (I, [P, I64, I64, I, U, QP, P, P, SZ, P]),
+        "fp8_mlp_workspace_bytes": (SZ, [I64, I64, I64, I]),
+        "fp8_mlp_fwd": (I, [P, P, P, I64, I64, I64, I, P, P, I, P, P, QP, QP, QP, QP, P, P, P, SZ, P]),
         "fp8_status_string": (ctypes.c_char_p, [I]),
         "fp8_last_error": (ctypes.c_char_p, []),
         "fp8_version": (ctypes.c_char_p, []),

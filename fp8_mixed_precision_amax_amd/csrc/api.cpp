@@ -166,7 +166,7 @@ constexpr int64_t kMaxContraction = int64_t(1) << 23;
 
 fp8_status do_gemm(const void* a, int fa, fp8k::GemmScale sa, const void* b, int fb, fp8k::GemmScale sb, int64_t I,
                    int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes, hipStream_t st,
-                   void* c_amax = nullptr) {
+                   void* c_amax = nullptr, void* c_gelu_keys = nullptr) {
     if (K >= kMaxContraction)
         return fail(FP8_ERR_SHAPE, "contraction length %lld: must be below 2^23", (long long)K);
     fp8k::GemmLaunch g;
@@ -183,6 +183,7 @@ fp8_status do_gemm(const void* a, int fa, fp8k::GemmScale sa, const void* b, int
     g.ws = ws;
     g.ws_bytes = ws_bytes;
     g.c_amax = static_cast<uint16_t*>(c_amax);
+    g.gelu_keys = static_cast<uint16_t*>(c_gelu_keys);
     return hip_status(fp8k::launch_gemm(g, st), "gemm launch");
 }
 
@@ -338,7 +339,7 @@ size_t fp8_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K) { return fp8k::
 
 static fp8_status gemm_checked(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb,
                                fp8_gemm_scale sb, int64_t I, int64_t J, int64_t K, void* c, void* ws, size_t ws_bytes,
-                               void* stream, void* c_amax) {
+                               void* stream, void* c_amax, void* c_gelu_keys = nullptr) {
     FP8_TRY(check_dims("gemm I x J", I, J));
     FP8_TRY(check_dims("gemm K", K, 128));
     if (K >= kMaxContraction) return fail(FP8_ERR_SHAPE, "contraction length %lld: must be below 2^23", (long long)K);
@@ -362,9 +363,14 @@ static fp8_status gemm_checked(const void* a, fp8_format fa, fp8_gemm_scale sa, 
         if (sa.group != 0) return fail(FP8_ERR_ENUM, "the output amax hand-off is for tensorwise GEMMs");
         FP8_TRY(check_ptr16("c_amax_partials", c_amax));
     }
+    if (c_gelu_keys) {
+        if (sa.group != 0 || fa != FP8_E4M3 || fb != FP8_E4M3)
+            return fail(FP8_ERR_ENUM, "the GELU amax keys are emitted by tensorwise E4M3 x E4M3 GEMMs");
+        FP8_TRY(check_ptr16("c_gelu_amax_partials", c_gelu_keys));
+    }
     return do_gemm(a, fa, fp8k::GemmScale{sa.scale_inv, sa.group, sa.stride_r, sa.stride_kb}, b, fb,
                    fp8k::GemmScale{sb.scale_inv, sb.group, sb.stride_r, sb.stride_kb}, I, J, K, c, ws, ws_bytes,
-                   static_cast<hipStream_t>(stream), c_amax);
+                   static_cast<hipStream_t>(stream), c_amax, c_gelu_keys);
 }
 
 fp8_status fp8_gemm(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb, fp8_gemm_scale sb,
@@ -377,6 +383,27 @@ fp8_status fp8_gemm_amax(const void* a, fp8_format fa, fp8_gemm_scale sa, const 
                          size_t ws_bytes, void* stream) {
     if (!c_amax_partials) return fail(FP8_ERR_NULL, "c_amax_partials is NULL");
     return gemm_checked(a, fa, sa, b, fb, sb, I, J, K, c, ws, ws_bytes, stream, c_amax_partials);
+}
+
+fp8_status fp8_gemm_gelu_amax(const void* a, fp8_format fa, fp8_gemm_scale sa, const void* b, fp8_format fb,
+                              fp8_gemm_scale sb, int64_t I, int64_t J, int64_t K, void* c,
+                              void* c_gelu_amax_partials, void* ws, size_t ws_bytes, void* stream) {
+    if (!c_gelu_amax_partials) return fail(FP8_ERR_NULL, "c_gelu_amax_partials is NULL");
+    return gemm_checked(a, fa, sa, b, fb, sb, I, J, K, c, ws, ws_bytes, stream, nullptr, c_gelu_amax_partials);
+}
+
+fp8_status fp8_quantize_gelu_from_amax(const void* x, int64_t rows, int64_t cols, fp8_format format,
+                                       unsigned layouts, const fp8_qtensor* out, const void* gelu_amax_partials,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    FP8_TRY(check_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out));
+    FP8_TRY(check_ptr16("gelu_amax_partials", gelu_amax_partials));
+    if (ws_bytes < kPartialBytes) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, kPartialBytes);
+    FP8_TRY(check_ptr16("ws", ws));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    FP8_TRY(hip_status(fp8k::launch_gelu_keys_to_partials(static_cast<const uint16_t*>(gelu_amax_partials),
+                                                          static_cast<uint16_t*>(ws), st),
+                       "GELU keys launch"));
+    return do_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out, nullptr, st, ws, 1);
 }
 
 fp8_status fp8_wcache_create(int64_t M, int64_t K, fp8_recipe recipe, const fp8_qtensor* bufs, fp8_wcache* out) {
@@ -461,59 +488,97 @@ static fp8_status check_amax_handoff(int recipe, const void* in, const void* out
     return FP8_OK;
 }
 
+// One forward pass, checked completely before anything is launched.
 // act 1: the linear's input is GELU(x) (x the pre-activation), quantized
-// without being written out
+// without being written out; x_amax_partials are then amax partials of
+// GELU(x).  y_gelu_keys (tensorwise): receives the GELU amax keys of Y.
+struct FwdCall {
+    const void* x;
+    int act;
+    const void* w;
+    int64_t N, K, M;
+    fp8_recipe recipe;
+    fp8_wcache cache;
+    int flag;
+    void* y;
+    const fp8_qtensor* saved_x;
+    const fp8_qtensor* w_q;
+    const void* x_amax_partials;
+    void* y_amax_partials;
+    void* y_gelu_keys;
+    void* ws;
+    size_t ws_bytes;
+    size_t ws_need;            // 0: the whole linear's workspace
+    const fp8_qtensor* wq;     // resolved by check_fwd
+};
+
+static fp8_status check_fwd(FwdCall& c) {
+    FP8_TRY(check_linear_common(c.N, c.K, c.M, c.recipe, c.ws, c.ws_bytes, c.ws_need));
+    if (c.flag != -1 && c.flag != 0 && c.flag != 1) return fail(FP8_ERR_ENUM, "is_first_microbatch must be -1, 0 or 1");
+    FP8_TRY(check_ptr16("x", c.x));
+    FP8_TRY(check_ptr16("y", c.y));
+    FP8_TRY(check_amax_handoff(c.recipe, c.x_amax_partials, c.y_amax_partials, "x_amax_partials", "y_amax_partials"));
+    FP8_TRY(check_amax_handoff(c.recipe, nullptr, c.y_gelu_keys, "", "y_gelu_keys"));
+    const int xsc = c.recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
+    const int wsc = c.recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_128x128 : FP8_SCALE_TENSOR;
+    FP8_TRY(check_quantize(c.x, c.N, c.K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, c.saved_x));
+    if (c.flag == -1) {
+        FP8_TRY(check_weight_q(c.w_q, c.recipe, true, true));
+        FP8_TRY(check_quantize(c.w, c.M, c.K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, c.w_q));
+        c.wq = c.w_q;
+    } else {
+        FP8_TRY(check_cache(c.cache, c.M, c.K, c.recipe));
+        if (c.flag == 1) {
+            FP8_TRY(check_quantize(c.w, c.M, c.K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, &c.cache->bufs));
+        } else if (!c.cache->valid) {
+            return fail(FP8_ERR_CACHE_EMPTY, "is_first_microbatch=False on an empty weight cache");
+        }
+        c.wq = &c.cache->bufs;
+    }
+    return FP8_OK;
+}
+
+static fp8_status run_fwd(const FwdCall& c, hipStream_t st) {
+    const int xsc = c.recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
+    const int wsc = c.recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_128x128 : FP8_SCALE_TENSOR;
+    const int64_t N = c.N, K = c.K, M = c.M;
+    const fp8_qtensor* wq = c.wq;
+    uint8_t* wsb = static_cast<uint8_t*>(c.ws);
+    void* gws = wsb + kPartialBytes;
+    const size_t gws_bytes = c.ws_bytes - kPartialBytes;
+    if (c.flag != 0 && c.recipe == FP8_RECIPE_TENSOR && c.act == 0 && !c.x_amax_partials) {
+        // X and W together: one amax launch and one cast launch; W's partials
+        // borrow the GEMM workspace (at least 4 KiB, checked above), which the
+        // forward GEMM only uses after
+        FP8_TRY(do_quantize_pair(c.x, N, K, c.saved_x, c.ws, c.w, M, K, wq, gws, st));
+    } else {
+        if (c.flag != 0)
+            FP8_TRY(do_quantize(c.w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, wq, c.ws, st));
+        FP8_TRY(do_quantize(c.x, N, K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, c.saved_x, c.ws, st,
+                            c.x_amax_partials, c.act));
+    }
+    if (c.flag == 1) {
+        c.cache->valid = 1;
+        c.cache->fills++;
+    }
+    const fp8_qtensor* sx = c.saved_x;
+    if (c.recipe == FP8_RECIPE_TENSOR)
+        return do_gemm(sx->q_row, FP8_E4M3, tensor_scale(sx->scale_inv), wq->q_row, FP8_E4M3,
+                       tensor_scale(wq->scale_inv), N, M, K, c.y, gws, gws_bytes, st, c.y_amax_partials,
+                       c.y_gelu_keys);
+    return do_gemm(sx->q_row, FP8_E4M3, block_scale(sx->scale_inv, 1, 1, N), wq->q_row, FP8_E4M3,
+                   block_scale(wq->scale_inv, 128, K / 128, 1), N, M, K, c.y, gws, gws_bytes, st);
+}
+
 // ws_need: 0 for the whole linear's workspace, else the forward's alone
 static fp8_status linear_fwd(const void* x, int act, const void* w, int64_t N, int64_t K, int64_t M,
                              fp8_recipe recipe, fp8_wcache cache, int flag, void* y, const fp8_qtensor* saved_x,
                              const fp8_qtensor* w_q, const void* x_amax_partials, void* y_amax_partials, void* ws,
                              size_t ws_bytes, void* stream, size_t ws_need = 0) {
-    FP8_TRY(check_linear_common(N, K, M, recipe, ws, ws_bytes, ws_need));
-    if (flag != -1 && flag != 0 && flag != 1) return fail(FP8_ERR_ENUM, "is_first_microbatch must be -1, 0 or 1");
-    FP8_TRY(check_ptr16("x", x));
-    FP8_TRY(check_ptr16("y", y));
-    FP8_TRY(check_amax_handoff(recipe, x_amax_partials, y_amax_partials, "x_amax_partials", "y_amax_partials"));
-    const int xsc = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
-    const int wsc = recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_128x128 : FP8_SCALE_TENSOR;
-    FP8_TRY(check_quantize(x, N, K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x));
-    const fp8_qtensor* wq = nullptr;
-    if (flag == -1) {
-        FP8_TRY(check_weight_q(w_q, recipe, true, true));
-        FP8_TRY(check_quantize(w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, w_q));
-        wq = w_q;
-    } else {
-        FP8_TRY(check_cache(cache, M, K, recipe));
-        if (flag == 1) {
-            FP8_TRY(check_quantize(w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, &cache->bufs));
-        } else if (!cache->valid) {
-            return fail(FP8_ERR_CACHE_EMPTY, "is_first_microbatch=False on an empty weight cache");
-        }
-        wq = &cache->bufs;
-    }
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t* wsb = static_cast<uint8_t*>(ws);
-    void* gws = wsb + kPartialBytes;
-    const size_t gws_bytes = ws_bytes - kPartialBytes;
-    if (flag != 0 && recipe == FP8_RECIPE_TENSOR && act == 0 && !x_amax_partials) {
-        // X and W together: one amax launch and one cast launch; W's partials
-        // borrow the GEMM workspace (at least 4 KiB, checked above), which the
-        // forward GEMM only uses after
-        FP8_TRY(do_quantize_pair(x, N, K, saved_x, ws, w, M, K, wq, gws, st));
-    } else {
-        if (flag != 0)
-            FP8_TRY(do_quantize(w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, wq, ws, st));
-        FP8_TRY(do_quantize(x, N, K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, saved_x, ws, st,
-                            x_amax_partials, act));
-    }
-    if (flag == 1) {
-        cache->valid = 1;
-        cache->fills++;
-    }
-    if (recipe == FP8_RECIPE_TENSOR)
-        return do_gemm(saved_x->q_row, FP8_E4M3, tensor_scale(saved_x->scale_inv), wq->q_row, FP8_E4M3,
-                       tensor_scale(wq->scale_inv), N, M, K, y, gws, gws_bytes, st, y_amax_partials);
-    return do_gemm(saved_x->q_row, FP8_E4M3, block_scale(saved_x->scale_inv, 1, 1, N), wq->q_row, FP8_E4M3,
-                   block_scale(wq->scale_inv, 128, K / 128, 1), N, M, K, y, gws, gws_bytes, st);
+    FwdCall c{x, act, w, N, K, M, recipe, cache, flag, y, saved_x, w_q, x_amax_partials, y_amax_partials, nullptr,
+              ws, ws_bytes, ws_need, nullptr};
+    FP8_TRY(check_fwd(c));
+    return run_fwd(c, static_cast<hipStream_t>(stream));
 }
 
 fp8_status fp8_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, int64_t M, fp8_recipe recipe,
@@ -547,6 +612,51 @@ fp8_status fp8_linear_fwd_gelu(const void* x_pre, const void* w, int64_t N, int6
                                void* stream) {
     return linear_fwd(x_pre, 1, w, N, K, M, recipe, cache, flag, y, saved_x, w_q, nullptr, y_amax_partials, ws,
                       ws_bytes, stream);
+}
+
+// The MLP block's forward: the up projection writes the pre-activation A and,
+// tensorwise, the GELU amax keys of A; the down projection's input GELU(A)
+// is then quantized in one pass (its amax from the keys).
+constexpr size_t kGeluKeyBytes = 4 * kPartialBytes;
+
+size_t fp8_mlp_workspace_bytes(int64_t N, int64_t D, int64_t H, fp8_recipe recipe) {
+    (void)recipe;
+    if (!dim_ok(N) || !dim_ok(D) || !dim_ok(H)) return 0;
+    const size_t a = linear_fwd_ws_bytes(N, D, H), b = linear_fwd_ws_bytes(N, H, D);
+    return kGeluKeyBytes + kPartialBytes + (a > b ? a : b);
+}
+
+fp8_status fp8_mlp_fwd(const void* x, const void* w1, const void* w2, int64_t N, int64_t D, int64_t H,
+                       fp8_recipe recipe, fp8_wcache cache1, fp8_wcache cache2, int flag, void* a, void* y,
+                       const fp8_qtensor* saved_x1, const fp8_qtensor* w1_q, const fp8_qtensor* saved_x2,
+                       const fp8_qtensor* w2_q, const void* x_amax_partials, void* y_amax_partials, void* ws,
+                       size_t ws_bytes, void* stream) {
+    FP8_TRY(check_linear_dims(N, D, H, recipe));
+    FP8_TRY(check_linear_dims(N, H, D, recipe));
+    const size_t need = fp8_mlp_workspace_bytes(N, D, H, recipe);
+    if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    FP8_TRY(check_ptr16("ws", ws));
+    if (a == y) return fail(FP8_ERR_SHAPE, "a and y must be different buffers");
+    const bool keys = recipe == FP8_RECIPE_TENSOR;
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    void* kbuf = wsb;                                   // GELU amax keys of A
+    void* pbuf = wsb + kGeluKeyBytes;                   // amax partials of GELU(A)
+    void* lws = wsb + kGeluKeyBytes + kPartialBytes;    // the linears' workspace
+    const size_t lws_bytes = ws_bytes - kGeluKeyBytes - kPartialBytes;
+    FwdCall up{x, 0, w1, N, D, H, recipe, cache1, flag, a, saved_x1, w1_q, x_amax_partials, nullptr,
+               keys ? kbuf : nullptr, lws, lws_bytes, linear_fwd_ws_bytes(N, D, H), nullptr};
+    FwdCall down{a, 1, w2, N, H, D, recipe, cache2, flag, y, saved_x2, w2_q, keys ? pbuf : nullptr,
+                 y_amax_partials, nullptr, lws, lws_bytes, linear_fwd_ws_bytes(N, H, D), nullptr};
+    FP8_TRY(check_fwd(up));
+    FP8_TRY(check_fwd(down));
+    if (cache1 && cache1 == cache2) return fail(FP8_ERR_CACHE_MISMATCH, "the two linears need their own caches");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    FP8_TRY(run_fwd(up, st));
+    if (keys)
+        FP8_TRY(hip_status(fp8k::launch_gelu_keys_to_partials(static_cast<const uint16_t*>(kbuf),
+                                                              static_cast<uint16_t*>(pbuf), st),
+                           "GELU keys launch"));
+    return run_fwd(down, st);
 }
 
 // act 2: the incoming gradient is dGELU(dy, y_pre): dy the gradient of

@@ -9,6 +9,7 @@
 // order, applies the tensorwise factor (block-scaled partials already carry
 // theirs) and rounds to bf16.
 #include "device.hpp"
+#include "gelu_keys.hpp"
 #include "gemm_common.hpp"
 #include "internal.hpp"
 
@@ -16,13 +17,16 @@ namespace fp8k {
 
 // Sum split-K partials in split order, apply the tensorwise factor, bf16.
 // With amax_part, also one partial max |bf16 C| per block (block 0 zeroes the
-// slots no block owns).
+// slots no block owns); with gelu_keys, the four GELU amax keys of C per
+// block likewise (gelu_keys.hpp).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t n4,
                                                             int64_t IJ, const float* sa, const float* sb,
                                                             int tensorwise, uint16_t* __restrict__ c,
-                                                            uint16_t* __restrict__ amax_part) {
+                                                            uint16_t* __restrict__ amax_part,
+                                                            uint16_t* __restrict__ gelu_keys) {
     const float t = tensorwise ? sa[0] * sb[0] : 1.0f;
     uint32_t amx = 0;
+    GeluKeys gk;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
         float4 s = reinterpret_cast<const float4*>(part)[i];
         for (int z = 1; z < splits; z++) {
@@ -36,6 +40,31 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
         reinterpret_cast<uint2*>(c)[i] = w;
         amx = pkmax_u16(amx, pkmax_u16(mag2(w.x), mag2(w.y)));
+        if (gelu_keys) {
+            gk.add(w.x);
+            gk.add(w.y);
+        }
+    }
+    if (gelu_keys) {
+        __shared__ uint32_t kred[kGeluKeyArrays][4];
+        uint32_t k[kGeluKeyArrays];
+        gk.fold(k);
+#pragma unroll
+        for (int q = 0; q < kGeluKeyArrays; q++) k[q] = wave_max_u32(k[q]);
+        if ((threadIdx.x & 63) == 0)
+#pragma unroll
+            for (int q = 0; q < kGeluKeyArrays; q++) kred[q][threadIdx.x >> 6] = k[q];
+        __syncthreads();
+        if (threadIdx.x < kGeluKeyArrays) {
+            const int q = (int)threadIdx.x;
+            uint32_t r = kred[q][0];
+            for (int w = 1; w < 4; w++) r = r > kred[q][w] ? r : kred[q][w];
+            gelu_keys[q * kMaxAmaxPartials + blockIdx.x] = (uint16_t)r;
+        }
+        if (blockIdx.x == 0)
+            for (int p = (int)gridDim.x + (int)threadIdx.x; p < kMaxAmaxPartials; p += 256)
+#pragma unroll
+                for (int q = 0; q < kGeluKeyArrays; q++) gelu_keys[q * kMaxAmaxPartials + p] = 0;
     }
     if (amax_part) {
         __shared__ uint32_t red[4];
@@ -94,7 +123,7 @@ hipError_t launch_gemm(const GemmLaunch& l, hipStream_t stream) {
     if (blocks > kMaxAmaxPartials) blocks = kMaxAmaxPartials;   // one amax partial per block
     hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const float*>(l.ws), splits, n4, l.I * l.J, l.sa.sinv, l.sb.sinv, block ? 0 : 1,
-                       static_cast<uint16_t*>(l.c), block ? nullptr : l.c_amax);
+                       static_cast<uint16_t*>(l.c), block ? nullptr : l.c_amax, block ? nullptr : l.gelu_keys);
     return hipGetLastError();
 }
 

@@ -43,6 +43,7 @@
 //    4 KiB LDS slice (chunk-major, (row ^ 2 chunk) swizzle: conflict-free
 //    writes and reads) and stores whole 128-byte row segments.
 #include "device.hpp"
+#include "gelu_keys.hpp"
 #include "gemm_common.hpp"
 #include "internal.hpp"
 
@@ -76,6 +77,8 @@ struct Args {
     int splits, tiles_i, tiles_j, kpairs, items;   // kpairs: contraction blocks of 128
     int gi;               // tile rows per raster group
     uint16_t* amax_part;  // optional: one partial max |bf16 C| per workgroup, zeros after
+    uint16_t* gelu_keys;  // KEYS: the four GELU amax key arrays (gelu_keys.hpp), one slot
+                          // per workgroup, zeros after
 };
 
 struct Item {
@@ -116,7 +119,7 @@ __device__ __forceinline__ void wait_vm_n(int n) {
     else wait_vm<0>();
 }
 
-template <int FA, int FB, bool NT>
+template <int FA, int FB, bool NT, bool KEYS = false>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     // separate objects: the epilogue's LDS traffic never aliases the stages
     __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
@@ -238,6 +241,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     // max |bf16| of the outputs this lane wrote (two packed 16-bit
     // magnitudes; NaN magnitudes exceed +Inf's, so NaN propagates)
     uint32_t amx = 0;
+    GeluKeys gk;   // KEYS: what the quantize of GELU(C) needs instead of an amax pass
 
     // write one item's accumulators; returns the vector-memory stores issued
     auto epilogue = [&](const Item& it) __attribute__((always_inline)) -> int {
@@ -273,6 +277,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
                     w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
                     w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
                     amx = pkmax_u16(amx, pkmax_u16(mag2(w.x), mag2(w.y)));
+                    if constexpr (KEYS) {
+                        gk.add(w.x);
+                        gk.add(w.y);
+                    }
                     const int chunk = nj * 4 + q;
                     const uint32_t wa = wbase + (uint32_t)(chunk * 512 + ((frow ^ (2 * chunk)) << 4));
                     asm volatile("ds_write_b64 %0, %1" : : "v"(wa), "v"(w) : "memory");
@@ -405,6 +413,30 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
         if (blockIdx.x == 0)
             for (int p = (int)gridDim.x + (int)threadIdx.x; p < kMaxAmaxPartials; p += NW * 64) g.amax_part[p] = 0;
     }
+    if constexpr (KEYS) {
+        // the same reduction for the four GELU keys (all max-reducible)
+        uint32_t k[kGeluKeyArrays];
+        gk.fold(k);
+#pragma unroll
+        for (int q = 0; q < kGeluKeyArrays; q++) k[q] = wave_max_u32(k[q]);
+        uint32_t* red = reinterpret_cast<uint32_t*>(sepi) + NW;
+        __syncthreads();
+        if (lane == 0)
+#pragma unroll
+            for (int q = 0; q < kGeluKeyArrays; q++) red[q * NW + wave] = k[q];
+        __syncthreads();
+        if (threadIdx.x < kGeluKeyArrays) {
+            const int q = (int)threadIdx.x;
+            uint32_t r = red[q * NW];
+#pragma unroll
+            for (int w = 1; w < NW; w++) r = r > red[q * NW + w] ? r : red[q * NW + w];
+            g.gelu_keys[q * kMaxAmaxPartials + blockIdx.x] = (uint16_t)r;
+        }
+        if (blockIdx.x == 0)
+            for (int p = (int)gridDim.x + (int)threadIdx.x; p < kMaxAmaxPartials; p += NW * 64)
+#pragma unroll
+                for (int q = 0; q < kGeluKeyArrays; q++) g.gelu_keys[q * kMaxAmaxPartials + p] = 0;
+    }
 }
 
 }  // namespace tensor
@@ -438,6 +470,7 @@ hipError_t launch_gemm_tensor(const GemmLaunch& l, int splits, hipStream_t strea
     g.items = g.tiles_i * g.tiles_j * splits;
     // the split-K reduce emits the amax of a split output
     g.amax_part = splits == 1 ? l.c_amax : nullptr;
+    g.gelu_keys = splits == 1 ? l.gelu_keys : nullptr;
     // an XCD's 32 concurrent items cover 8 tile rows x 4 columns when the
     // output is wide (8192 x 8192 x 16384: 955 -> 820 us against groups of
     // 2), 16 x 2 when it has few tile columns (131072 x 512 x 2048: 139 us
@@ -449,6 +482,13 @@ hipError_t launch_gemm_tensor(const GemmLaunch& l, int splits, hipStream_t strea
 #define FP8K_LAUNCH(FA, FB)                                                                                     \
     if (nt) hipLaunchKernelGGL((gemm_tensor_kernel<FA, FB, true>), dim3(grid), dim3(NW * 64), 0, stream, g);  \
     else hipLaunchKernelGGL((gemm_tensor_kernel<FA, FB, false>), dim3(grid), dim3(NW * 64), 0, stream, g)
+    if (g.gelu_keys) {
+        // the keys are emitted for E4M3 x E4M3 only (the forward GEMM)
+        if (l.fa != 0 || l.fb != 0) return hipErrorInvalidValue;
+        if (nt) hipLaunchKernelGGL((gemm_tensor_kernel<0, 0, true, true>), dim3(grid), dim3(NW * 64), 0, stream, g);
+        else hipLaunchKernelGGL((gemm_tensor_kernel<0, 0, false, true>), dim3(grid), dim3(NW * 64), 0, stream, g);
+        return hipGetLastError();
+    }
     if (l.fa == 0 && l.fb == 0) { FP8K_LAUNCH(0, 0); }
     else if (l.fa == 1 && l.fb == 0) { FP8K_LAUNCH(1, 0); }
     else if (l.fa == 0 && l.fb == 1) { FP8K_LAUNCH(0, 1); }

@@ -69,6 +69,8 @@ struct GemmLaunch {
     size_t ws_bytes;
     uint16_t* c_amax;   // tensorwise, optional: kMaxAmaxPartials partial maxima of |C|
                         // (bf16 magnitude bits, 0 in unused slots)
+    uint16_t* gelu_keys = nullptr;   // tensorwise E4M3 x E4M3, optional: the GELU amax keys
+                                     // of C (4 arrays of kMaxAmaxPartials slots, gelu_keys.hpp)
 };
 
 // Split-K factor the GEMM launcher will use for this shape (1 = none) and
@@ -84,6 +86,11 @@ int gemm_block_wide_splits(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm_block_wide(const GemmLaunch& l, int splits, hipStream_t stream);
 size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
+
+// Quantize of GELU(x) whose amax comes from the GELU keys its producer wrote
+// (gelu_keys.hpp): one small kernel turns the keys into amax partials of
+// GELU(x) in `partials` (kMaxAmaxPartials slots), then the cast pass alone.
+hipError_t launch_gelu_keys_to_partials(const uint16_t* keys, uint16_t* partials, hipStream_t stream);
 
 // Scratch of the entry point that allocates nothing (noalloc.hip): a device
 // array of kNoallocScratchBytes per GPU; *out receives the current device's

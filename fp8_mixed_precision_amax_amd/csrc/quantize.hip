@@ -581,7 +581,7 @@ hipError_t launch_act_quantize(const QuantizeLaunch& q, CastArgs& a, hipStream_t
     hipError_t e = act_tables(stream, t);
     if (e != hipSuccess) return e;
     a.act_tab = q.act == 1 ? static_cast<const void*>(t.gelu) : static_cast<const void*>(t.dgelu);
-    if (q.scaling == 0) {
+    if (q.scaling == 0 && !q.partial_given) {
         // about two workgroups per CU: each one copies the table to LDS first
         const int64_t n16 = q.rows * q.cols / 8;
         int64_t g = (n16 + (int64_t)kAmaxThreads * 16 - 1) / ((int64_t)kAmaxThreads * 16);

@@ -243,6 +243,55 @@ fp8_status fp8_gemm_amax(const void* a, fp8_format format_a, fp8_gemm_scale scal
                          int64_t I, int64_t J, int64_t K, void* c_bf16, void* c_amax_partials,
                          void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * GELU amax hand-off.  In the MLP block the down projection's input is
+ * GELU(A), A the up projection's bf16 output, and amax(GELU(A)) is not a
+ * function of amax(A): GELU falls to its minimum near -0.7518 and rises on
+ * either side.  The GEMM that writes A therefore emits four 16-bit keys per
+ * workgroup instead of one magnitude:
+ *   gelu amax partials  FP8_GELU_AMAX_PARTIALS_BYTES of device memory
+ *                  (16-byte aligned): four arrays of 2048 16-bit slots,
+ *                  each reduced by unsigned maximum, 0 meaning "nothing":
+ *     [0]  (v ^ 0x8000) for the largest non-negative value (bf16 pattern v,
+ *          compared as signed 16-bit; NaN above +Inf)
+ *     [1]  the largest bf16 pattern as unsigned (>= 0xFF80: a -Inf or a
+ *          negative NaN is present, whose GELU is NaN)
+ *     [2]  (v - 0xBF41) mod 2^16 maximised: at or above 0xC0BF it names the
+ *          smallest value in [-0.75, 0)
+ *     [3]  the complement of (v - 0xBF41) mod 2^16 minimised: at or above
+ *          0xBF41 (complemented: a minimum at or below 0x40BE) it names the
+ *          largest value below -0.75
+ * -0.75 is the smallest bf16 value above GELU's minimiser; bf16(GELU) is
+ * monotone on each side of it, so max |GELU| over the tensor is the largest
+ * of |GELU| at the (at most three) values the keys name, or NaN.
+ * Written by fp8_gemm_gelu_amax (and inside fp8_mlp_fwd), read by
+ * fp8_quantize_gelu_from_amax (and inside fp8_mlp_fwd).
+ */
+#define FP8_GELU_AMAX_PARTIALS_BYTES 16384
+
+/*
+ * fp8_gemm for tensorwise E4M3 x E4M3 operands (FP8_ERR_ENUM otherwise) that
+ * also writes the GELU amax partials of its bf16 output C into
+ * c_gelu_amax_partials (NULL is FP8_ERR_NULL).  C is bitwise fp8_gemm's.
+ */
+fp8_status fp8_gemm_gelu_amax(const void* a, fp8_format format_a, fp8_gemm_scale scale_a,
+                              const void* b, fp8_format format_b, fp8_gemm_scale scale_b,
+                              int64_t I, int64_t J, int64_t K, void* c_bf16, void* c_gelu_amax_partials,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Tensorwise quantize of GELU(x) (as fp8_quantize_gelu) whose amax comes from
+ * the GELU amax partials the producer of x wrote: the cast pass alone (plus
+ * one single-workgroup kernel that reads the 16 KiB of keys).  ws: at least
+ * fp8_quantize_workspace_bytes(rows, cols, FP8_SCALE_TENSOR) bytes.  The
+ * bytes and scales equal fp8_quantize_gelu's on the same x; results are
+ * undefined if the partials do not describe x.
+ */
+fp8_status fp8_quantize_gelu_from_amax(const void* x_bf16, int64_t rows, int64_t cols, fp8_format format,
+                                       unsigned layouts, const fp8_qtensor* out,
+                                       const void* gelu_amax_partials, void* ws, size_t ws_bytes,
+                                       void* stream);
+
 /* ---------------------------- weight cache --------------------------- */
 
 /*
@@ -305,6 +354,35 @@ fp8_status fp8_linear_bwd(const void* dy_bf16, int64_t N, int64_t K, int64_t M, 
                           const fp8_qtensor* dy_q, void* dx_bf16, void* dw_bf16,
                           const void* dy_amax_partials, void* dx_amax_partials,
                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The MLP block's forward in one call: the up projection A [N, H] = X W1^T
+ * (X [N, D], W1 [H, D]) and the down projection Y [N, D] = GELU(A) W2^T
+ * (W2 [D, H]), each exactly as fp8_linear_fwd / fp8_linear_fwd_gelu would
+ * compute it (bitwise the same A, Y, saved inputs and quantized weights).
+ * Under the tensorwise recipe the up projection's GEMM writes the GELU amax
+ * partials of A into the workspace, so the quantize of GELU(A) is the cast
+ * pass alone instead of an amax pass plus the cast ("Native FP8 MLP
+ * reconstruction", discussion: quantization reductions are the work the
+ * model's FLOP estimate leaves out); under the block recipe that quantize is
+ * one pass already.  A is written out because the backward pass
+ * (fp8_linear_bwd on the down projection, fp8_linear_bwd_dgelu on the up
+ * projection) needs it.  cache1 / cache2 follow the weight-cache protocol of
+ * fp8_linear_fwd with one is_first_microbatch flag for both; saved_x1,
+ * w1_q, saved_x2, w2_q are those of the two linears.  x_amax_partials
+ * (tensorwise, may be NULL) replaces X's amax pass; y_amax_partials (may be
+ * NULL) receives Y's.  Every check of both linears happens before anything
+ * is enqueued.  ws: fp8_mlp_workspace_bytes bytes (0 for invalid sizes).
+ */
+size_t fp8_mlp_workspace_bytes(int64_t N, int64_t D, int64_t H, fp8_recipe recipe);
+fp8_status fp8_mlp_fwd(const void* x_bf16, const void* w1_bf16, const void* w2_bf16,
+                       int64_t N, int64_t D, int64_t H, fp8_recipe recipe,
+                       fp8_wcache cache1, fp8_wcache cache2, int is_first_microbatch,
+                       void* a_bf16, void* y_bf16,
+                       const fp8_qtensor* saved_x1, const fp8_qtensor* w1_q,
+                       const fp8_qtensor* saved_x2, const fp8_qtensor* w2_q,
+                       const void* x_amax_partials, void* y_amax_partials,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------- forward without any allocation ------------------ */
 
