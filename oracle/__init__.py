@@ -79,6 +79,8 @@ def _load():
         "orc_gelu_f32_array": (None, [P, I64, P]),
         "orc_gelu_grad_f32_array": (None, [P, I64, P]),
         "orc_dgelu_array": (None, [P, P, I64, P]),
+        "orc_gemm_bf16": (None, [P, P, I64, I64, I64, P, P, P]),
+        "orc_gemm_bf16_sampled": (None, [P, P, I64, P, P, I64, P, P]),
         "orc_num_threads": (I, []),
         "orc_set_num_threads": (None, [I]),
     }
@@ -447,3 +449,48 @@ def linear_bwd_dgelu(dh, a, ctx):
     """The first linear of an MLP block, backward: its incoming gradient is
     dGELU(dH, A), dH the gradient of GELU's output, A its pre-activation."""
     return linear_bwd(dgelu(dh, a), ctx)
+
+
+# --------------------------------------------------------------------------
+# The BF16 comparator linear (the pages' baseline: the same linears without
+# FP8, "Native FP8 MLP reconstruction", isolated-linear table).  Every GEMM
+# multiplies bf16 values exactly and sums in fp32 with k ascending; outputs
+# are rounded to bf16.  Transposed operands are plain numpy transposes.
+# --------------------------------------------------------------------------
+
+def gemm_bf16(A, B, want_f32=False):
+    """C[i][j] = bf16(sum_k A[i][k] B[j][k]); A [I, K], B [J, K] bf16 bits."""
+    A = _c(A, np.uint16)
+    B = _c(B, np.uint16)
+    I, K = A.shape
+    J, K2 = B.shape
+    assert K == K2
+    C = np.empty((I, J), np.uint16)
+    C32 = np.empty((I, J), np.float32) if want_f32 else None
+    work = np.empty((I + J) * K, np.float32)
+    _load().orc_gemm_bf16(_p(A), _p(B), I, J, K, _p(C), _p(C32), _p(work))
+    return (C, C32) if want_f32 else C
+
+
+def gemm_bf16_sampled(A, B, ii, jj, want_f32=False):
+    A = _c(A, np.uint16)
+    B = _c(B, np.uint16)
+    K = A.shape[1]
+    ii = _c(ii, np.int64)
+    jj = _c(jj, np.int64)
+    out = np.empty(ii.shape, np.uint16)
+    out32 = np.empty(ii.shape, np.float32) if want_f32 else None
+    _load().orc_gemm_bf16_sampled(_p(A), _p(B), K, _p(ii), _p(jj), ii.size, _p(out), _p(out32))
+    return (out, out32) if want_f32 else out
+
+
+def linear_bf16_fwd(x, w):
+    """Y = X W^T in BF16: x [N, K], w [M, K] bf16 bits."""
+    return gemm_bf16(x, w)
+
+
+def linear_bf16_bwd(dy, x, w):
+    """dX = dY W (contraction over M), dW = dY^T X (over N)."""
+    dx = gemm_bf16(dy, np.ascontiguousarray(np.asarray(w).T))
+    dw = gemm_bf16(np.ascontiguousarray(np.asarray(dy).T), np.ascontiguousarray(np.asarray(x).T))
+    return dx, dw

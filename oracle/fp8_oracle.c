@@ -36,6 +36,8 @@
  *    GELU and GELU' each rounded once to fp32 from an fp64 evaluation; the
  *    activation is bf16(fl32(GELU(x))), the gradient through it
  *    bf16(fl32(dy * fl32(GELU'(x)))); NaN results are the quiet NaN 0x7FC0.
+ *  - the BF16 comparator linear (the pages' baseline) multiplies bf16
+ *    operands exactly, sums in fp32 with k ascending and rounds to bf16.
  *
  * Compile with -O2 -ffp-contract=off (no fused multiply-add, no fast-math).
  * Parity status: every function below is pinned by the CPU test-suite
@@ -531,6 +533,57 @@ void orc_gemm_block_sampled(const uint8_t* A, int fa, const float* sA, int64_t g
             float pt = p * t;
             acc = acc + pt;
         }
+        if (out32) out32[n_] = acc;
+        out[n_] = orc_bf16_rne(acc);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* BF16 comparator GEMM (the pages' baseline, "Native FP8 MLP           */
+/* reconstruction", isolated-linear table: the same linears in BF16).   */
+/* C[i][j] = bf16_rne(sum_k A[i][k] * B[j][k]), A [I, K] and B [J, K]    */
+/* bf16 bit patterns, both K-contiguous; every product of two bf16       */
+/* values is exact in fp32 (8-bit significands), and the sum runs in    */
+/* fp32 with k ascending, one add per product.                          */
+/* work: caller-provided fp32 scratch of (I + J) * K floats.            */
+/* ------------------------------------------------------------------ */
+
+void orc_gemm_bf16(const uint16_t* A, const uint16_t* B, int64_t I, int64_t J, int64_t K,
+                   uint16_t* C, float* C32, float* work) {
+    float* Ad = work;                   /* [I, K] */
+    float* Bt = work + I * K;           /* [K, J]: B transposed */
+    for (int64_t i = 0; i < I * K; i++) Ad[i] = orc_dec_bf16(A[i]);
+    for (int64_t j = 0; j < J; j++)
+        for (int64_t k = 0; k < K; k++) Bt[k * J + j] = orc_dec_bf16(B[j * K + k]);
+    #pragma omp parallel
+    {
+        float* acc = (float*)malloc(sizeof(float) * (size_t)J);
+        #pragma omp for schedule(static)
+        for (int64_t i = 0; i < I; i++) {
+            for (int64_t j = 0; j < J; j++) acc[j] = 0.0f;
+            for (int64_t k = 0; k < K; k++) {
+                float a = Ad[i * K + k];
+                const float* brow = Bt + k * J;
+                for (int64_t j = 0; j < J; j++) acc[j] += a * brow[j];
+            }
+            for (int64_t j = 0; j < J; j++) {
+                if (C32) C32[i * J + j] = acc[j];
+                C[i * J + j] = orc_bf16_rne(acc[j]);
+            }
+        }
+        free(acc);
+    }
+}
+
+/* Sampled outputs of the same GEMM: out[n] = C[ii[n]][jj[n]]. */
+void orc_gemm_bf16_sampled(const uint16_t* A, const uint16_t* B, int64_t K, const int64_t* ii,
+                           const int64_t* jj, int64_t n, uint16_t* out, float* out32) {
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n_ = 0; n_ < n; n_++) {
+        const uint16_t* a = A + ii[n_] * K;
+        const uint16_t* b = B + jj[n_] * K;
+        float acc = 0.0f;
+        for (int64_t k = 0; k < K; k++) acc += orc_dec_bf16(a[k]) * orc_dec_bf16(b[k]);
         if (out32) out32[n_] = acc;
         out[n_] = orc_bf16_rne(acc);
     }
