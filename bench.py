@@ -751,33 +751,55 @@ def chain_times(fp8, torch, synth, N, steps, warmup, dev):
             "value_handoff": round(flops / (res[True] / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
 
 
-def bf16_comparator(torch, synth, N, steps, warmup, dev):
+BF16_PEAK_TFLOPS = 2500.0   # dense BF16 matrix-core peak of the MI355X (vendor figure)
+
+
+def bf16_comparator(fp8, torch, synth, N, steps, warmup, reps, dev):
     """The pages' baseline: the same two linears' forward + backward in BF16
-    (no quantization), each product one hipBLASLt GEMM through torch.mm with
-    bf16 output; right-hand operands contiguous."""
+    (no quantization), timed two ways: this library's hand-written BF16
+    matrix-core GEMMs (fp8_bf16_linear_fwd / _bwd; W and the gradients' left
+    operands read output-major, no transposed copies) and hipBLASLt through
+    torch.mm (right-hand operands contiguous).  Per GEMM of the hand-written
+    path: time and fraction of the dense BF16 peak."""
     ops = []
     for idx, (K, M) in enumerate(SHAPES):
         x, w, dy = synth.operands_on_device(N, K, M, seed=idx, device=dev)
-        ops.append((x, w, w.t().contiguous(), dy))
+        ops.append((x, w, w.t().contiguous(), dy, fp8.Bf16Linear(N, K, M, device=dev),
+                    torch.empty((N, M), dtype=torch.bfloat16, device=dev),
+                    torch.empty((N, K), dtype=torch.bfloat16, device=dev),
+                    torch.empty((M, K), dtype=torch.bfloat16, device=dev)))
 
-    def step():
-        for x, w, wt, dy in ops:
+    def step_lib():
+        for x, w, wt, dy, lin, y, dx, dw in ops:
             torch.mm(x, wt)            # Y = X W^T
             torch.mm(dy, w)            # dX = dY W
             torch.mm(dy.t(), x)        # dW = dY^T X
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    def step_own():
+        for x, w, wt, dy, lin, y, dx, dw in ops:
+            lin.forward(x, w, y=y)
+            lin.backward(dy, x, w, dx=dx, dw=dw)
+
     flops = sum(6 * N * K * M for K, M in SHAPES)
-    return {"workload": "the same two linears in BF16 (hipBLASLt via torch.mm, bf16 out), N=%d" % N,
-            "ms_per_step": round(ms, 4), "value": round(flops / (ms / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
+    t_lib = timing_groups(torch, step_lib, steps, warmup)["ms"]
+    t_own = timing_groups(torch, step_own, steps, warmup)["ms"]
+    gemms = {}
+    for x, w, wt, dy, lin, y, dx, dw in ops:
+        K, M = lin.K, lin.M
+        tag = "%dx%d" % (K, M)
+        for name, fn, fl in (("fprop", lambda: fp8.bf16_gemm(x, w, 0, 0, out=y), 2 * N * K * M),
+                             ("dgrad", lambda: fp8.bf16_gemm(dy, w, 0, 1, out=dx), 2 * N * K * M),
+                             ("wgrad", lambda: fp8.bf16_gemm(dy, x, 1, 1, out=dw), 2 * N * K * M)):
+            ms = _ms(torch, fn, reps)
+            gemms["%s_%s" % (name, tag)] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                                            "bf16_peak_frac": round(fl / ms / 1e9 / BF16_PEAK_TFLOPS, 3)}
+    del ops
+    torch.cuda.empty_cache()
+    return {"workload": "the same two linears in BF16, N=%d: hand-written BF16 matrix-core GEMMs, and hipBLASLt "
+                        "via torch.mm (bf16 out)" % N,
+            "ms_per_step": round(t_own, 4), "value": round(flops / (t_own / 1e3) / 1e12, 2),
+            "ms_per_step_hipblaslt": round(t_lib, 4), "value_hipblaslt": round(flops / (t_lib / 1e3) / 1e12, 2),
+            "unit": "TFLOP/s", "gemms": gemms}
 
 
 def delayed_quant_times(fp8, torch, synth, N, reps, dev):
@@ -879,11 +901,31 @@ def mlp_gelu_times(fp8, torch, synth, N, steps, warmup, reps, dev):
         l2.backward(dy, dx=dhid, dw=dw2)
         l1.backward(fp8.dgelu(dhid, ya, out=h), dx=dx1, dw=dw1)
 
+    mlp = fp8.Fp8Mlp(N, K1, M1, device=dev)
+
+    def handoff():
+        # forward in one call: the up projection's GEMM hands the GELU amax
+        # keys of its output to the down projection's input quantize
+        mlp.forward(x, w1, w2, y=y2, a=ya)
+        dh_, _ = mlp.down.backward(dy, dx=dhid, dw=dw2)
+        mlp.up.backward(dhid, dx=dx1, dw=dw1, gelu_input=ya)
+
     flops = sum(6 * N * K * M for K, M in SHAPES)
-    bf, bu = _ms(torch, fused, steps, warmup), _ms(torch, unfused, steps, warmup)
-    res["block"] = {"ms_fused": round(bf, 4), "ms_unfused": round(bu, 4),
+    bf, bu, bh = _ms(torch, fused, steps, warmup), _ms(torch, unfused, steps, warmup), _ms(torch, handoff, steps, warmup)
+    # the down projection's input quantize alone: two passes, or the cast pass
+    # fed by the keys the up projection's GEMM wrote
+    keys = fp8.gelu_amax_partials(dev)
+    qx = fp8.QTensor(N, M1, fp8.SCALE_TENSOR, dev)
+    sx, sw = fp8.gemm_scale(l1.saved_x.scale_inv), fp8.gemm_scale(l1.w_q.scale_inv)
+    fp8.gemm(l1.saved_x.q_row, fp8.E4M3, sx, l1.w_q.q_row, fp8.E4M3, sw, out=ya, gelu_amax_out=keys)
+    q_two = _ms(torch, lambda: fp8.quantize_gelu(ya, fp8.E4M3, out=qx), reps)
+    q_one = _ms(torch, lambda: fp8.quantize_gelu(ya, fp8.E4M3, out=qx, gelu_amax_partials=keys), reps)
+    res["block"] = {"ms_fused": round(bf, 4), "ms_unfused": round(bu, 4), "ms_fused_gelu_handoff": round(bh, 4),
                     "tflops_fused": round(flops / (bf / 1e3) / 1e12, 2),
-                    "tflops_unfused": round(flops / (bu / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
+                    "tflops_unfused": round(flops / (bu / 1e3) / 1e12, 2),
+                    "tflops_fused_gelu_handoff": round(flops / (bh / 1e3) / 1e12, 2), "unit": "TFLOP/s",
+                    "gelu_quantize_two_pass_ms": round(q_two, 4), "gelu_quantize_from_keys_ms": round(q_one, 4),
+                    "gelu_quantize_from_keys_gbs": round(4 * n / q_one / 1e6, 1)}
     return res
 
 
@@ -1086,9 +1128,13 @@ def main():
               (chain["ms_per_step"], chain["ms_per_step_handoff"]), file=sys.stderr, flush=True)
     bf16 = None
     if not args.no_block:
-        bf16 = bf16_comparator(torch, synth, N, args.steps, args.warmup, dev)
+        bf16 = bf16_comparator(fp8, torch, synth, N, args.steps, args.warmup, args.reps, dev)
         bf16["fp8_speedup"] = round(bf16["ms_per_step"] / ms, 3)
-        print("bf16 comparator: %.4f ms/step (FP8 step %.2fx faster)" % (bf16["ms_per_step"], bf16["fp8_speedup"]),
+        bf16["fp8_speedup_vs_hipblaslt"] = round(bf16["ms_per_step_hipblaslt"] / ms, 3)
+        print("bf16 comparator: hand-written %.4f ms/step, hipBLASLt %.4f ms/step (FP8 step %.2fx / %.2fx faster); "
+              "GEMMs %s" % (bf16["ms_per_step"], bf16["ms_per_step_hipblaslt"], bf16["fp8_speedup"],
+                            bf16["fp8_speedup_vs_hipblaslt"],
+                            ", ".join("%s %.0f" % (k, v["tflops"]) for k, v in bf16["gemms"].items())),
               file=sys.stderr, flush=True)
     delayed = None
     if not args.no_block:
@@ -1098,9 +1144,11 @@ def main():
     mlp = None
     if not args.no_block:
         mlp = mlp_gelu_times(fp8, torch, synth, N, args.steps, args.warmup, args.reps, dev)
-        print("MLP block with GELU: fused %.4f ms, unfused %.4f ms; GELU quantize fused %.4f ms, unfused %.4f ms" %
-              (mlp["block"]["ms_fused"], mlp["block"]["ms_unfused"], mlp["tensor"]["gelu_fused"]["ms"],
-               mlp["tensor"]["gelu_unfused"]["ms"]), file=sys.stderr, flush=True)
+        print("MLP block with GELU: fused %.4f ms, unfused %.4f ms, fused with the GELU amax hand-off %.4f ms; "
+              "GELU quantize fused %.4f ms, unfused %.4f ms, from the keys %.4f ms" %
+              (mlp["block"]["ms_fused"], mlp["block"]["ms_unfused"], mlp["block"]["ms_fused_gelu_handoff"],
+               mlp["tensor"]["gelu_fused"]["ms"], mlp["tensor"]["gelu_unfused"]["ms"],
+               mlp["block"]["gelu_quantize_from_keys_ms"]), file=sys.stderr, flush=True)
     configs = None
     stack = None
     if not args.no_block:

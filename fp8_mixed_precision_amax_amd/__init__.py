@@ -451,3 +451,57 @@ class Fp8Mlp:
         dh, dw2 = self.down.backward(dy, stream=stream)
         dx, dw1 = self.up.backward(dh, stream=stream, gelu_input=self.a)
         return dx, dw1, dw2
+
+
+# ------------------------------ BF16 comparator ------------------------------
+
+def bf16_gemm(a, b, a_layout=0, b_layout=0, I=None, J=None, out=None, stream=None):
+    """C [I, J] = bf16(sum_k A[i][k] B[j][k]) on the BF16 matrix cores
+    (fp8_bf16_gemm).  layout 0: the tensor is [rows, K] (contraction-major);
+    1: the tensor is [K, rows] (output-major)."""
+    L = lib()
+    for t in (a, b):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("operands must be contiguous 2-D bfloat16 tensors")
+    I = a.shape[0] if a_layout == 0 else a.shape[1]
+    K = a.shape[1] if a_layout == 0 else a.shape[0]
+    J = b.shape[0] if b_layout == 0 else b.shape[1]
+    Kb = b.shape[1] if b_layout == 0 else b.shape[0]
+    if K != Kb:
+        raise ValueError("contraction sizes differ")
+    with _on(stream):
+        if out is None:
+            out = torch.empty((I, J), dtype=torch.bfloat16, device=a.device)
+        wsb = L.fp8_bf16_gemm_workspace_bytes(I, J, K)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=a.device)
+        _lib.check(L.fp8_bf16_gemm(_ptr(a), a_layout, _ptr(b), b_layout, I, J, K, _ptr(out), _ptr(ws), wsb,
+                                   _stream(stream)))
+    return out
+
+
+class Bf16Linear:
+    """The BF16 comparator linear Y = X W^T (fp8_bf16_linear_fwd / _bwd):
+    no quantization, hand-written BF16 matrix-core GEMMs."""
+
+    def __init__(self, N, K, M, device="cuda"):
+        self.N, self.K, self.M = N, K, M
+        n = lib().fp8_bf16_linear_workspace_bytes(N, K, M)
+        self.ws, self.ws_bytes = torch.empty(max(n, 16), dtype=torch.uint8, device=device), n
+
+    def forward(self, x, w, y=None, stream=None):
+        with _on(stream):
+            if y is None:
+                y = torch.empty((self.N, self.M), dtype=torch.bfloat16, device=x.device)
+        _lib.check(lib().fp8_bf16_linear_fwd(_ptr(x), _ptr(w), self.N, self.K, self.M, _ptr(y), _ptr(self.ws),
+                                             self.ws_bytes, _stream(stream)))
+        return y
+
+    def backward(self, dy, x, w, dx=None, dw=None, stream=None):
+        with _on(stream):
+            if dx is None:
+                dx = torch.empty((self.N, self.K), dtype=torch.bfloat16, device=dy.device)
+            if dw is None:
+                dw = torch.empty((self.M, self.K), dtype=torch.bfloat16, device=dy.device)
+        _lib.check(lib().fp8_bf16_linear_bwd(_ptr(dy), _ptr(x), _ptr(w), self.N, self.K, self.M, _ptr(dx), _ptr(dw),
+                                             _ptr(self.ws), self.ws_bytes, _stream(stream)))
+        return dx, dw

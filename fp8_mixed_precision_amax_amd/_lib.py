@@ -30,7 +30,8 @@ EXPORTS = [
     "fp8_wcache_destroy", "fp8_linear_workspace_bytes", "fp8_linear_fwd", "fp8_linear_bwd",
     "fp8_gelu", "fp8_dgelu", "fp8_quantize_gelu", "fp8_quantize_dgelu", "fp8_linear_fwd_gelu",
     "fp8_linear_bwd_dgelu", "fp8_linear_fwd_noalloc", "fp8_gemm_gelu_amax", "fp8_quantize_gelu_from_amax",
-    "fp8_mlp_workspace_bytes", "fp8_mlp_fwd",
+    "fp8_mlp_workspace_bytes", "fp8_mlp_fwd", "fp8_bf16_gemm_workspace_bytes", "fp8_bf16_gemm",
+    "fp8_bf16_linear_workspace_bytes", "fp8_bf16_linear_fwd", "fp8_bf16_linear_bwd",
     "fp8_status_string", "fp8_last_error", "fp8_version",
 ]
 
@@ -93,6 +94,11 @@ def load():
         "fp8_gemm_gelu_amax": (I, [P, I, GemmScaleC, P, I, GemmScaleC, I64, I64, I64, P, P, P, SZ, P]),
         "fp8_quantize_gelu_from_amax": (I, [P, I64, I64, I, U, QP, P, P, SZ, P]),
         "fp8_mlp_workspace_bytes": (SZ, [I64, I64, I64, I]),
+        "fp8_bf16_gemm_workspace_bytes": (SZ, [I64, I64, I64]),
+        "fp8_bf16_gemm": (I, [P, I, P, I, I64, I64, I64, P, P, SZ, P]),
+        "fp8_bf16_linear_workspace_bytes": (SZ, [I64, I64, I64]),
+        "fp8_bf16_linear_fwd": (I, [P, P, I64, I64, I64, P, P, SZ, P]),
+        "fp8_bf16_linear_bwd": (I, [P, P, P, I64, I64, I64, P, P, P, SZ, P]),
         "fp8_mlp_fwd": (I, [P, P, P, I64, I64, I64, I, P, P, I, P, P, QP, QP, QP, QP, P, P, P, SZ, P]),
         "fp8_status_string": (ctypes.c_char_p, [I]),
         "fp8_last_error": (ctypes.c_char_p, []),

@@ -614,6 +614,65 @@ fp8_status fp8_linear_fwd_gelu(const void* x_pre, const void* w, int64_t N, int6
                       ws_bytes, stream);
 }
 
+// ------------------------- BF16 comparator -------------------------
+
+size_t fp8_bf16_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K) { return fp8k::gemm_bf16_ws_bytes(I, J, K); }
+
+static fp8_status bf16_gemm_checked(const void* a, int la, const void* b, int lb, int64_t I, int64_t J, int64_t K,
+                                    void* c, void* ws, size_t ws_bytes) {
+    FP8_TRY(check_dims("bf16 gemm I x J", I, J));
+    FP8_TRY(check_dims("bf16 gemm K", K, 128));
+    if ((la != 0 && la != 1) || (lb != 0 && lb != 1)) return fail(FP8_ERR_ENUM, "operand layout must be 0 or 1");
+    FP8_TRY(check_ptr16("a", a));
+    FP8_TRY(check_ptr16("b", b));
+    FP8_TRY(check_ptr16("c", c));
+    const size_t need = fp8k::gemm_bf16_ws_bytes(I, J, K);
+    if (need) {
+        if (ws_bytes < need) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+        FP8_TRY(check_ptr16("ws", ws));
+    }
+    return FP8_OK;
+}
+
+static fp8_status bf16_gemm_run(const void* a, int la, const void* b, int lb, int64_t I, int64_t J, int64_t K, void* c,
+                                void* ws, hipStream_t st) {
+    fp8k::Bf16GemmLaunch l{a, la, b, lb, I, J, K, c, ws};
+    return hip_status(fp8k::launch_gemm_bf16(l, st), "bf16 gemm launch");
+}
+
+fp8_status fp8_bf16_gemm(const void* a, int a_layout, const void* b, int b_layout, int64_t I, int64_t J, int64_t K,
+                         void* c, void* ws, size_t ws_bytes, void* stream) {
+    FP8_TRY(bf16_gemm_checked(a, a_layout, b, b_layout, I, J, K, c, ws, ws_bytes));
+    return bf16_gemm_run(a, a_layout, b, b_layout, I, J, K, c, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t fp8_bf16_linear_workspace_bytes(int64_t N, int64_t K, int64_t M) {
+    if (!dim_ok(N) || !dim_ok(K) || !dim_ok(M)) return 0;
+    const size_t a = fp8k::gemm_bf16_ws_bytes(N, M, K), b = fp8k::gemm_bf16_ws_bytes(N, K, M),
+                 c = fp8k::gemm_bf16_ws_bytes(M, K, N);
+    const size_t m = a > b ? a : b;
+    return m > c ? m : c;
+}
+
+fp8_status fp8_bf16_linear_fwd(const void* x, const void* w, int64_t N, int64_t K, int64_t M, void* y, void* ws,
+                               size_t ws_bytes, void* stream) {
+    FP8_TRY(bf16_gemm_checked(x, 0, w, 0, N, M, K, y, ws, ws_bytes));
+    return bf16_gemm_run(x, 0, w, 0, N, M, K, y, ws, static_cast<hipStream_t>(stream));
+}
+
+fp8_status fp8_bf16_linear_bwd(const void* dy, const void* x, const void* w, int64_t N, int64_t K, int64_t M,
+                               void* dx, void* dw, void* ws, size_t ws_bytes, void* stream) {
+    if (!dx && !dw) return fail(FP8_ERR_NULL, "dx and dw are both NULL");
+    // dX [N, K] = dY W: contraction over M, W read output-major
+    if (dx) FP8_TRY(bf16_gemm_checked(dy, 0, w, 1, N, K, M, dx, ws, ws_bytes));
+    // dW [M, K] = dY^T X: contraction over N, both read output-major
+    if (dw) FP8_TRY(bf16_gemm_checked(dy, 1, x, 1, M, K, N, dw, ws, ws_bytes));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dx) FP8_TRY(bf16_gemm_run(dy, 0, w, 1, N, K, M, dx, ws, st));
+    if (dw) FP8_TRY(bf16_gemm_run(dy, 1, x, 1, M, K, N, dw, ws, st));
+    return FP8_OK;
+}
+
 // The MLP block's forward: the up projection writes the pre-activation A and,
 // tensorwise, the GELU amax keys of A; the down projection's input GELU(A)
 // is then quantized in one pass (its amax from the keys).

@@ -81,6 +81,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
 }
 
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t I, int64_t J, const float* sa,
+                                const float* sb, uint16_t* c, hipStream_t stream) {
+    const int64_t n4 = I * J / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > kMaxAmaxPartials) blocks = kMaxAmaxPartials;
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, splits, n4, I * J, sa,
+                       sb, sa ? 1 : 0, c, nullptr, nullptr);
+    return hipGetLastError();
+}
+
 int cu_count() {
     static int cache[64] = {0};
     int dev = 0;

@@ -87,6 +87,29 @@ hipError_t launch_gemm_block_wide(const GemmLaunch& l, int splits, hipStream_t s
 size_t gemm_ws_bytes(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm(const GemmLaunch& g, hipStream_t stream);
 
+// Deterministic sum of split-K fp32 partials [splits][I][J] in slice order,
+// times fl32(sa[0] * sb[0]) when sa is given (tensorwise), rounded to bf16
+// into c (gemm.hip).
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t I, int64_t J, const float* sa,
+                                const float* sb, uint16_t* c, hipStream_t stream);
+
+// BF16 GEMM (gemm_bf16.hip): C [I, J] = bf16(sum_k A[i][k] B[j][k]) with
+// fp32 accumulation; layout 0: contraction-major (A[i][k] at i*K + k),
+// 1: output-major (A[i][k] at k*I + i; B likewise with J).  ws: split-K
+// partials, gemm_bf16_ws_bytes.
+struct Bf16GemmLaunch {
+    const void* a;
+    int ta;
+    const void* b;
+    int tb;
+    int64_t I, J, K;
+    void* c;
+    void* ws;
+};
+int gemm_bf16_splits(int64_t I, int64_t J, int64_t K);
+size_t gemm_bf16_ws_bytes(int64_t I, int64_t J, int64_t K);
+hipError_t launch_gemm_bf16(const Bf16GemmLaunch& l, hipStream_t stream);
+
 // Quantize of GELU(x) whose amax comes from the GELU keys its producer wrote
 // (gelu_keys.hpp): one small kernel turns the keys into amax partials of
 // GELU(x) in `partials` (kMaxAmaxPartials slots), then the cast pass alone.

@@ -384,6 +384,39 @@ fp8_status fp8_mlp_fwd(const void* x_bf16, const void* w1_bf16, const void* w2_b
                        const void* x_amax_partials, void* y_amax_partials,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* --------------------------- BF16 comparator --------------------------- */
+
+/*
+ * The pages' baseline: the same linears in BF16 without any quantization
+ * ("Native FP8 MLP reconstruction", isolated-linear table, the compiled
+ * BF16 column), here as hand-written BF16 matrix-core GEMMs so that the
+ * FP8/BF16 speed ratio on this GPU comes from this library's own kernels.
+ *
+ * C [I, J] = bf16(sum_k A[i][k] B[j][k]), bf16 operands, fp32 accumulation,
+ * round to nearest even.  Operand layouts (no transposed copies needed):
+ *   layout 0  contraction-major: A[i][k] at a[i * K + k]  (B: b[j * K + k])
+ *   layout 1  output-major:      A[i][k] at a[k * I + i]  (B: b[k * J + j])
+ * I, J, K positive multiples of 128; pointers 16-byte aligned; ws holds the
+ * split-K partial sums (fp8_bf16_gemm_workspace_bytes; 0 when none).
+ */
+size_t fp8_bf16_gemm_workspace_bytes(int64_t I, int64_t J, int64_t K);
+fp8_status fp8_bf16_gemm(const void* a_bf16, int a_layout, const void* b_bf16, int b_layout,
+                         int64_t I, int64_t J, int64_t K, void* c_bf16, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/*
+ * BF16 linear: forward Y [N, M] = X [N, K] W [M, K]^T; backward dX [N, K] =
+ * dY W (W read output-major) and dW [M, K] = dY^T X (both read output-major);
+ * dx or dw may be NULL to skip that product.  Workspace from
+ * fp8_bf16_linear_workspace_bytes (covers all three products).
+ */
+size_t fp8_bf16_linear_workspace_bytes(int64_t N, int64_t K, int64_t M);
+fp8_status fp8_bf16_linear_fwd(const void* x_bf16, const void* w_bf16, int64_t N, int64_t K, int64_t M,
+                               void* y_bf16, void* ws, size_t ws_bytes, void* stream);
+fp8_status fp8_bf16_linear_bwd(const void* dy_bf16, const void* x_bf16, const void* w_bf16,
+                               int64_t N, int64_t K, int64_t M, void* dx_bf16, void* dw_bf16,
+                               void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------- forward without any allocation ------------------ */
 
 /*
