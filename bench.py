@@ -701,11 +701,27 @@ def latency_small(fp8, torch, synth, dev, steps=500, warmup=50):
     microseconds, median of five timing groups."""
     layers, _ = workload_layers(fp8, torch, synth, "linear_512x512_n1024", dev)
     L = layers[0]
-    t = timing_groups(torch, linear_step(layers), steps, warmup)
+    step = linear_step(layers)
+    t = timing_groups(torch, step, steps, warmup)
+    # the same step captured once into a HIP graph (the library allocates
+    # nothing and records no memset, so its launches capture as they are)
+    # and replayed: what launch overhead the eager step pays
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    tg = timing_groups(torch, graph.replay, steps, warmup)
+    flops = 6 * L["N"] * L["K"] * L["M"]
     return {"workload": "fp8 linear 512->512 fwd+bwd, N=1024, tensorwise current scaling",
             "us_per_step": round(t["ms"] * 1e3, 2), "us_per_step_mean": round(t["mean_ms"] * 1e3, 2),
-            "steps": steps, "value": round(6 * L["N"] * L["K"] * L["M"] / (t["ms"] / 1e3) / 1e12, 2),
-            "unit": "TFLOP/s"}
+            "us_per_step_graph": round(tg["ms"] * 1e3, 2),
+            "steps": steps, "value": round(flops / (t["ms"] / 1e3) / 1e12, 2),
+            "value_graph": round(flops / (tg["ms"] / 1e3) / 1e12, 2), "unit": "TFLOP/s"}
 
 
 def chain_times(fp8, torch, synth, N, steps, warmup, dev):
@@ -1097,7 +1113,8 @@ def main():
     quant_gbs = sum(s["bytes"] for s in q) / sum(s["ms"] for s in q) / 1e6
     dom = max(stages, key=lambda s: s["ms"])     # the stage (one library call) that takes longest
     lat = latency_small(fp8, torch, synth, dev)
-    print("512->512 at N=1024: %.2f us/step" % lat["us_per_step"], file=sys.stderr, flush=True)
+    print("512->512 at N=1024: %.2f us/step eager, %.2f us/step replayed from a HIP graph" %
+          (lat["us_per_step"], lat["us_per_step_graph"]), file=sys.stderr, flush=True)
     block = None
     if not args.no_block:
         # the same two linears under block scaling (X, dY 1x128; W 128x128)
