@@ -454,7 +454,9 @@ def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8
     the cache and the amax hand-off on the edges without a GELU between
     (block p's output is block p+1's input; block p+1's input gradient is
     block p's output gradient).  The weight gradients of the last cycle are
-    compared bitwise across the runs."""
+    compared bitwise across the runs.  The hand-off run also takes each
+    block's forward in one call (fp8_mlp_fwd), whose up projection hands the
+    GELU amax keys of its output to the down projection's input quantize."""
     d, h = 512, 2048
     R = fp8.RECIPE_BLOCK if recipe == "block" else fp8.RECIPE_TENSOR
     g = torch.Generator(device=dev)
@@ -478,16 +480,22 @@ def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8
         dg = torch.empty((N, h), dtype=torch.bfloat16, device=dev)
         dh = [torch.empty((N, d), dtype=torch.bfloat16, device=dev) for _ in range(2)]
         pa, pb = (fp8.amax_partials(dev), fp8.amax_partials(dev)) if handoff else (None, None)
+        mlps = [fp8.Fp8Mlp(N, d, h, R, dev, up=lins[2 * p], down=lins[2 * p + 1]) for p in range(layers)] \
+            if handoff else None
 
         def cycle():
             for mb in range(mbs):
                 flag = (mb == 0) if cached else None
                 x = xs[mb]
                 for p in range(layers):
-                    lins[2 * p].forward(x, weights[2 * p], y=pre[p], is_first_microbatch=flag,
-                                        x_amax=pa if (handoff and p > 0) else None)
-                    lins[2 * p + 1].forward(pre[p], weights[2 * p + 1], y=hid[p], is_first_microbatch=flag,
-                                            gelu=True, y_amax=pa if (handoff and p + 1 < layers) else None)
+                    if handoff:
+                        mlps[p].forward(x, weights[2 * p], weights[2 * p + 1], y=hid[p], a=pre[p],
+                                        is_first_microbatch=flag, x_amax=pa if p > 0 else None,
+                                        y_amax=pa if p + 1 < layers else None)
+                    else:
+                        lins[2 * p].forward(x, weights[2 * p], y=pre[p], is_first_microbatch=flag)
+                        lins[2 * p + 1].forward(pre[p], weights[2 * p + 1], y=hid[p], is_first_microbatch=flag,
+                                                gelu=True)
                     x = hid[p]
                 g_in = dys[mb]
                 for p in reversed(range(layers)):
@@ -507,7 +515,7 @@ def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8
         torch.cuda.synchronize()
         res[mode] = e0.elapsed_time(e1) / cycles
         final[mode] = [w.clone() for w in dws]
-        del lins, pre, hid, dws, dg, dh, pa, pb
+        del lins, mlps, pre, hid, dws, dg, dh, pa, pb
         torch.cuda.empty_cache()
     flops = mbs * sum(6 * N * K * M for K, M in shapes)
     out = {"workload": "%d x (512->2048, GELU, 2048->512), N=%d per microbatch, %d microbatches per cycle, %s"

@@ -225,11 +225,9 @@ def quantize_gelu(x, fmt, scaling=SCALE_TENSOR, layouts=LAYOUT_ROW | LAYOUT_COL,
     with _on(stream):
         if out is None:
             out = QTensor(R, C, scaling, _dev(x), row=bool(layouts & LAYOUT_ROW), col=bool(layouts & LAYOUT_COL))
-        wsb = L.fp8_quantize_workspace_bytes(R, C, SCALE_TENSOR)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
         oc = out.c()
         _lib.check(L.fp8_quantize_gelu_from_amax(_ptr(x), R, C, fmt, layouts, ctypes.byref(oc),
-                                                 _ptr(gelu_amax_partials), _ptr(ws), wsb, _stream(stream)))
+                                                 _ptr(gelu_amax_partials), _stream(stream)))
     return out
 
 
@@ -420,10 +418,12 @@ class Fp8Mlp:
     backward through the two linears' entry points (the up projection's
     gradient quantize applies GELU')."""
 
-    def __init__(self, N, D, H, recipe=RECIPE_TENSOR, device="cuda", cache=False):
+    def __init__(self, N, D, H, recipe=RECIPE_TENSOR, device="cuda", cache=False, up=None, down=None):
+        """up / down: existing Fp8Linear objects of the two linears (their
+        buffers and caches are then shared with direct calls on them)."""
         self.N, self.D, self.H, self.recipe = N, D, H, recipe
-        self.up = Fp8Linear(N, D, H, recipe, device, cache)
-        self.down = Fp8Linear(N, H, D, recipe, device, cache)
+        self.up = up if up is not None else Fp8Linear(N, D, H, recipe, device, cache)
+        self.down = down if down is not None else Fp8Linear(N, H, D, recipe, device, cache)
         n = lib().fp8_mlp_workspace_bytes(N, D, H, recipe)
         self.ws, self.ws_bytes = torch.empty(max(n, 16), dtype=torch.uint8, device=device), n
         self.a = None

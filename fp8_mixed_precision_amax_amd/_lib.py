@@ -92,7 +92,7 @@ def load():
         "fp8_linear_bwd_dgelu": (I, [P, P, I64, I64, I64, I, QP, P, QP, QP, P, P, P, P, SZ, P]),
         "fp8_linear_fwd_noalloc": (I, [P, P, I64, I64, I64, I, P, I, P, QP, QP, P, P, P]),
         "fp8_gemm_gelu_amax": (I, [P, I, GemmScaleC, P, I, GemmScaleC, I64, I64, I64, P, P, P, SZ, P]),
-        "fp8_quantize_gelu_from_amax": (I, [P, I64, I64, I, U, QP, P, P, SZ, P]),
+        "fp8_quantize_gelu_from_amax": (I, [P, I64, I64, I, U, QP, P, P]),
         "fp8_mlp_workspace_bytes": (SZ, [I64, I64, I64, I]),
         "fp8_bf16_gemm_workspace_bytes": (SZ, [I64, I64, I64]),
         "fp8_bf16_gemm": (I, [P, I, P, I, I64, I64, I64, P, P, SZ, P]),

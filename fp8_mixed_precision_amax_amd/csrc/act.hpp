@@ -87,6 +87,13 @@ __device__ __forceinline__ float dgelu_closed(uint32_t b) {
     return __uint_as_float(r);
 }
 
+// bf16 GELU of one bf16 pattern b: the table (LDS or global), or the closed
+// forms outside it.
+__device__ __forceinline__ uint32_t gelu_one(uint32_t b, const uint16_t* tab) {
+    if (((b & 0x7FFFu) - kActLo) >= kActHalf) return gelu_closed(b);
+    return tab[((b & 0x7FFFu) - kActLo) + ((b & 0x8000u) ? kActHalf : 0u)];
+}
+
 // fp32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.
 __device__ __forceinline__ uint32_t bf16_rne_canon(float v) {
     const uint32_t u = __float_as_uint(v);

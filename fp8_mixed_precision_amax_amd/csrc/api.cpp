@@ -112,7 +112,8 @@ fp8_status hip_status(hipError_t e, const char* what) {
 // act: 0 quantize x; 1 quantize GELU(x); 2 quantize dGELU(x, x2)
 static fp8k::QuantizeLaunch quantize_launch(const void* x, int64_t rows, int64_t cols, int format, int scaling,
                                             unsigned layouts, const fp8_qtensor* out, void* ws,
-                                            const void* given_amax, int act, const void* x2) {
+                                            const void* given_amax, int act, const void* x2,
+                                            const void* gelu_keys = nullptr) {
     fp8k::QuantizeLaunch q;
     q.x = x;
     q.rows = rows;
@@ -132,13 +133,15 @@ static fp8k::QuantizeLaunch quantize_launch(const void* x, int64_t rows, int64_t
     q.hist_len = 0;
     q.act = act;
     q.x2 = x2;
+    q.gelu_keys = static_cast<const uint16_t*>(gelu_keys);
     return q;
 }
 
 fp8_status do_quantize(const void* x, int64_t rows, int64_t cols, int format, int scaling, unsigned layouts,
                        const fp8_qtensor* out, void* ws, hipStream_t st, const void* given_amax = nullptr,
-                       int act = 0, const void* x2 = nullptr) {
-    const fp8k::QuantizeLaunch q = quantize_launch(x, rows, cols, format, scaling, layouts, out, ws, given_amax, act, x2);
+                       int act = 0, const void* x2 = nullptr, const void* gelu_keys = nullptr) {
+    const fp8k::QuantizeLaunch q =
+        quantize_launch(x, rows, cols, format, scaling, layouts, out, ws, given_amax, act, x2, gelu_keys);
     return hip_status(fp8k::launch_quantize(q, st), "quantize launch");
 }
 
@@ -394,16 +397,11 @@ fp8_status fp8_gemm_gelu_amax(const void* a, fp8_format fa, fp8_gemm_scale sa, c
 
 fp8_status fp8_quantize_gelu_from_amax(const void* x, int64_t rows, int64_t cols, fp8_format format,
                                        unsigned layouts, const fp8_qtensor* out, const void* gelu_amax_partials,
-                                       void* ws, size_t ws_bytes, void* stream) {
+                                       void* stream) {
     FP8_TRY(check_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out));
     FP8_TRY(check_ptr16("gelu_amax_partials", gelu_amax_partials));
-    if (ws_bytes < kPartialBytes) return fail(FP8_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, kPartialBytes);
-    FP8_TRY(check_ptr16("ws", ws));
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    FP8_TRY(hip_status(fp8k::launch_gelu_keys_to_partials(static_cast<const uint16_t*>(gelu_amax_partials),
-                                                          static_cast<uint16_t*>(ws), st),
-                       "GELU keys launch"));
-    return do_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out, nullptr, st, ws, 1);
+    return do_quantize(x, rows, cols, format, FP8_SCALE_TENSOR, layouts, out, nullptr,
+                       static_cast<hipStream_t>(stream), nullptr, 1, nullptr, gelu_amax_partials);
 }
 
 fp8_status fp8_wcache_create(int64_t M, int64_t K, fp8_recipe recipe, const fp8_qtensor* bufs, fp8_wcache* out) {
@@ -490,8 +488,9 @@ static fp8_status check_amax_handoff(int recipe, const void* in, const void* out
 
 // One forward pass, checked completely before anything is launched.
 // act 1: the linear's input is GELU(x) (x the pre-activation), quantized
-// without being written out; x_amax_partials are then amax partials of
-// GELU(x).  y_gelu_keys (tensorwise): receives the GELU amax keys of Y.
+// without being written out; x_gelu_keys (tensorwise, optional) are then the
+// GELU amax keys of x, which replace the amax pass.  y_gelu_keys
+// (tensorwise): receives the GELU amax keys of Y.
 struct FwdCall {
     const void* x;
     int act;
@@ -506,6 +505,7 @@ struct FwdCall {
     const void* x_amax_partials;
     void* y_amax_partials;
     void* y_gelu_keys;
+    const void* x_gelu_keys;
     void* ws;
     size_t ws_bytes;
     size_t ws_need;            // 0: the whole linear's workspace
@@ -518,7 +518,9 @@ static fp8_status check_fwd(FwdCall& c) {
     FP8_TRY(check_ptr16("x", c.x));
     FP8_TRY(check_ptr16("y", c.y));
     FP8_TRY(check_amax_handoff(c.recipe, c.x_amax_partials, c.y_amax_partials, "x_amax_partials", "y_amax_partials"));
-    FP8_TRY(check_amax_handoff(c.recipe, nullptr, c.y_gelu_keys, "", "y_gelu_keys"));
+    FP8_TRY(check_amax_handoff(c.recipe, c.x_gelu_keys, c.y_gelu_keys, "x_gelu_keys", "y_gelu_keys"));
+    if (c.x_gelu_keys && (c.act != 1 || c.x_amax_partials))
+        return fail(FP8_ERR_ENUM, "GELU amax keys serve the quantize of GELU(x) alone");
     const int xsc = c.recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_1x128 : FP8_SCALE_TENSOR;
     const int wsc = c.recipe == FP8_RECIPE_BLOCK ? FP8_SCALE_BLOCK_128x128 : FP8_SCALE_TENSOR;
     FP8_TRY(check_quantize(c.x, c.N, c.K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, c.saved_x));
@@ -555,7 +557,7 @@ static fp8_status run_fwd(const FwdCall& c, hipStream_t st) {
         if (c.flag != 0)
             FP8_TRY(do_quantize(c.w, M, K, FP8_E4M3, wsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, wq, c.ws, st));
         FP8_TRY(do_quantize(c.x, N, K, FP8_E4M3, xsc, FP8_LAYOUT_ROW | FP8_LAYOUT_COL, c.saved_x, c.ws, st,
-                            c.x_amax_partials, c.act));
+                            c.x_amax_partials, c.act, nullptr, c.x_gelu_keys));
     }
     if (c.flag == 1) {
         c.cache->valid = 1;
@@ -576,7 +578,7 @@ static fp8_status linear_fwd(const void* x, int act, const void* w, int64_t N, i
                              const fp8_qtensor* w_q, const void* x_amax_partials, void* y_amax_partials, void* ws,
                              size_t ws_bytes, void* stream, size_t ws_need = 0) {
     FwdCall c{x, act, w, N, K, M, recipe, cache, flag, y, saved_x, w_q, x_amax_partials, y_amax_partials, nullptr,
-              ws, ws_bytes, ws_need, nullptr};
+              nullptr, ws, ws_bytes, ws_need, nullptr};
     FP8_TRY(check_fwd(c));
     return run_fwd(c, static_cast<hipStream_t>(stream));
 }
@@ -682,7 +684,7 @@ size_t fp8_mlp_workspace_bytes(int64_t N, int64_t D, int64_t H, fp8_recipe recip
     (void)recipe;
     if (!dim_ok(N) || !dim_ok(D) || !dim_ok(H)) return 0;
     const size_t a = linear_fwd_ws_bytes(N, D, H), b = linear_fwd_ws_bytes(N, H, D);
-    return kGeluKeyBytes + kPartialBytes + (a > b ? a : b);
+    return kGeluKeyBytes + (a > b ? a : b);
 }
 
 fp8_status fp8_mlp_fwd(const void* x, const void* w1, const void* w2, int64_t N, int64_t D, int64_t H,
@@ -698,23 +700,18 @@ fp8_status fp8_mlp_fwd(const void* x, const void* w1, const void* w2, int64_t N,
     if (a == y) return fail(FP8_ERR_SHAPE, "a and y must be different buffers");
     const bool keys = recipe == FP8_RECIPE_TENSOR;
     uint8_t* wsb = static_cast<uint8_t*>(ws);
-    void* kbuf = wsb;                                   // GELU amax keys of A
-    void* pbuf = wsb + kGeluKeyBytes;                   // amax partials of GELU(A)
-    void* lws = wsb + kGeluKeyBytes + kPartialBytes;    // the linears' workspace
-    const size_t lws_bytes = ws_bytes - kGeluKeyBytes - kPartialBytes;
+    void* kbuf = wsb;                       // GELU amax keys of A
+    void* lws = wsb + kGeluKeyBytes;        // the linears' workspace
+    const size_t lws_bytes = ws_bytes - kGeluKeyBytes;
     FwdCall up{x, 0, w1, N, D, H, recipe, cache1, flag, a, saved_x1, w1_q, x_amax_partials, nullptr,
-               keys ? kbuf : nullptr, lws, lws_bytes, linear_fwd_ws_bytes(N, D, H), nullptr};
-    FwdCall down{a, 1, w2, N, H, D, recipe, cache2, flag, y, saved_x2, w2_q, keys ? pbuf : nullptr,
-                 y_amax_partials, nullptr, lws, lws_bytes, linear_fwd_ws_bytes(N, H, D), nullptr};
+               keys ? kbuf : nullptr, nullptr, lws, lws_bytes, linear_fwd_ws_bytes(N, D, H), nullptr};
+    FwdCall down{a, 1, w2, N, H, D, recipe, cache2, flag, y, saved_x2, w2_q, nullptr, y_amax_partials, nullptr,
+                 keys ? kbuf : nullptr, lws, lws_bytes, linear_fwd_ws_bytes(N, H, D), nullptr};
     FP8_TRY(check_fwd(up));
     FP8_TRY(check_fwd(down));
     if (cache1 && cache1 == cache2) return fail(FP8_ERR_CACHE_MISMATCH, "the two linears need their own caches");
     hipStream_t st = static_cast<hipStream_t>(stream);
     FP8_TRY(run_fwd(up, st));
-    if (keys)
-        FP8_TRY(hip_status(fp8k::launch_gelu_keys_to_partials(static_cast<const uint16_t*>(kbuf),
-                                                              static_cast<uint16_t*>(pbuf), st),
-                           "GELU keys launch"));
     return run_fwd(down, st);
 }
 

@@ -16,12 +16,9 @@
 //   act_table_kernel  fills both tables
 //   gelu_kernel       y = GELU(x), 16-byte loads and stores, table in LDS
 //   dgelu_kernel      dx = dy * GELU'(x), likewise
-//   gelu_keys_kernel  amax partials of GELU(y) from the GELU amax keys a GEMM
-//                     wrote about y (gelu_keys.hpp)
 #include <mutex>
 
 #include "act.hpp"
-#include "gelu_keys.hpp"
 #include "internal.hpp"
 
 namespace fp8k {
@@ -120,67 +117,6 @@ __global__ __launch_bounds__(kActThreads) void dgelu_kernel(const uint4* __restr
         for (int u = 0; u < 4; u++) st_nt16(dx + i + u * stride, dgelu8(d[u], v[u], tab));
     }
     for (; i < n16; i += stride) st_nt16(dx + i, dgelu8(ld_nt16(dy + i), ld_nt16(x + i), tab));
-}
-
-// bf16 GELU of one bf16 value: the table, or the closed forms outside it.
-__device__ __forceinline__ uint32_t gelu_one(uint32_t b, const uint16_t* __restrict__ tab) {
-    if (act_outside(b)) return gelu_closed(b);
-    return tab[((b & 0x7FFFu) - kActLo) + ((b & 0x8000u) ? kActHalf : 0u)];
-}
-
-// One workgroup: reduce the four key arrays, evaluate GELU at the (at most
-// three) values they name, and write max |GELU| as magnitude bits into slot
-// 0 of the partials (the other slots 0) -- the form the cast pass reads.
-__global__ __launch_bounds__(256) void gelu_keys_kernel(const uint16_t* __restrict__ keys,
-                                                        uint16_t* __restrict__ partials,
-                                                        const uint16_t* __restrict__ gtab) {
-    __shared__ uint32_t red[kGeluKeyArrays][4];
-    uint32_t k[kGeluKeyArrays];
-#pragma unroll
-    for (int q = 0; q < kGeluKeyArrays; q++) {
-        uint32_t m = 0;
-        for (int s = (int)threadIdx.x; s < kMaxAmaxPartials; s += 256) {
-            const uint32_t v = keys[q * kMaxAmaxPartials + s];
-            m = m > v ? m : v;
-        }
-        k[q] = wave_max_u32(m);
-    }
-    if ((threadIdx.x & 63) == 0)
-#pragma unroll
-        for (int q = 0; q < kGeluKeyArrays; q++) red[q][threadIdx.x >> 6] = k[q];
-    __syncthreads();
-    for (int s = (int)threadIdx.x + 1; s < kMaxAmaxPartials; s += 256) partials[s] = 0;
-    if (threadIdx.x != 0) return;
-#pragma unroll
-    for (int q = 0; q < kGeluKeyArrays; q++)
-        for (int w = 1; w < 4; w++) red[q][0] = red[q][0] > red[q][w] ? red[q][0] : red[q][w];
-    const uint32_t p = red[0][0] ^ 0x8000u;       // back to int16 order: below 0x8000 is non-negative
-    const uint32_t v = red[1][0];
-    const uint32_t k2 = red[2][0];
-    const uint32_t k3 = (~red[3][0]) & 0xFFFFu;
-    uint32_t amax = 0;
-    if (p < 0x8000u) {
-        const uint32_t a = gelu_one(p, gtab) & 0x7FFFu;
-        amax = a > amax ? a : amax;
-    }
-    if (k2 >= 0xC0BFu) {                           // the smallest value in [-0.75, 0)
-        const uint32_t a = gelu_one((k2 + 0xBF41u) & 0xFFFFu, gtab) & 0x7FFFu;
-        amax = a > amax ? a : amax;
-    }
-    if (k3 <= 0x40BEu) {                           // the largest value below -0.75
-        const uint32_t a = gelu_one((k3 + 0xBF41u) & 0xFFFFu, gtab) & 0x7FFFu;
-        amax = a > amax ? a : amax;
-    }
-    if (v >= 0xFF80u) amax = 0x7FC0u;              // -Inf or a negative NaN: GELU is NaN there
-    partials[0] = (uint16_t)amax;
-}
-
-hipError_t launch_gelu_keys_to_partials(const uint16_t* keys, uint16_t* partials, hipStream_t stream) {
-    ActTables t;
-    hipError_t e = act_tables(stream, t);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gelu_keys_kernel, dim3(1), dim3(256), 0, stream, keys, partials, t.gelu);
-    return hipGetLastError();
 }
 
 // workgroups of the elementwise kernels: about four per CU, each reading its

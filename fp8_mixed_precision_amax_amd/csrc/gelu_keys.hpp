@@ -68,4 +68,29 @@ struct GeluKeys {
     }
 };
 
+// amax(GELU) as bf16 magnitude bits (NaN above +Inf) from the four reduced
+// keys k[0..3] in their stored form; gelu(b) returns the bf16 GELU of the
+// bf16 pattern b.
+template <class Gelu>
+__device__ __forceinline__ uint32_t gelu_amax_from_keys(const uint32_t k[kGeluKeyArrays], Gelu gelu) {
+    const uint32_t p = k[0] ^ 0x8000u;             // back to int16 order: below 0x8000 is non-negative
+    const uint32_t k2 = k[2];
+    const uint32_t k3 = (~k[3]) & 0xFFFFu;
+    uint32_t amax = 0;
+    if (p < 0x8000u) {
+        const uint32_t a = gelu(p) & 0x7FFFu;
+        amax = a > amax ? a : amax;
+    }
+    if (k2 >= 0xC0BFu) {                           // the smallest value in [-0.75, 0)
+        const uint32_t a = gelu((k2 + 0xBF41u) & 0xFFFFu) & 0x7FFFu;
+        amax = a > amax ? a : amax;
+    }
+    if (k3 <= 0x40BEu) {                           // the largest value below -0.75
+        const uint32_t a = gelu((k3 + 0xBF41u) & 0xFFFFu) & 0x7FFFu;
+        amax = a > amax ? a : amax;
+    }
+    if (k[1] >= 0xFF80u) amax = 0x7FC0u;           // -Inf or a negative NaN: GELU is NaN there
+    return amax;
+}
+
 }  // namespace fp8k

@@ -30,6 +30,8 @@ struct QuantizeLaunch {
     int act = 0;        // 0: quantize x; 1: quantize GELU(x); 2: quantize dGELU(x, x2), x the
                         // gradient of GELU's output and x2 its input (scaling 0 or 1 only)
     const void* x2 = nullptr;
+    const uint16_t* gelu_keys = nullptr;   // act 1, tensorwise: the GELU amax keys x's producer
+                                           // wrote (gelu_keys.hpp); the amax pass is skipped
 };
 
 int amax_partial_count(int64_t numel);
@@ -109,11 +111,6 @@ struct Bf16GemmLaunch {
 int gemm_bf16_splits(int64_t I, int64_t J, int64_t K);
 size_t gemm_bf16_ws_bytes(int64_t I, int64_t J, int64_t K);
 hipError_t launch_gemm_bf16(const Bf16GemmLaunch& l, hipStream_t stream);
-
-// Quantize of GELU(x) whose amax comes from the GELU keys its producer wrote
-// (gelu_keys.hpp): one small kernel turns the keys into amax partials of
-// GELU(x) in `partials` (kMaxAmaxPartials slots), then the cast pass alone.
-hipError_t launch_gelu_keys_to_partials(const uint16_t* keys, uint16_t* partials, hipStream_t stream);
 
 // Scratch of the entry point that allocates nothing (noalloc.hip): a device
 // array of kNoallocScratchBytes per GPU; *out receives the current device's

@@ -43,6 +43,7 @@
 //                         written out: each workgroup copies its table to
 //                         LDS once and then loops over tiles.
 #include "act.hpp"
+#include "gelu_keys.hpp"
 #include "device.hpp"
 #include "internal.hpp"
 
@@ -184,6 +185,8 @@ struct CastArgs {
     uint16_t* tile_amax;      // delayed only: amax of each 128x128 tile (bf16 magnitude bits)
     const uint16_t* x2;       // dGELU only: GELU's input [R, C]; x is the gradient of its output
     const void* act_tab;      // GELU / GELU' table (global memory), act_cast_kernel only
+    const uint16_t* gelu_keys; // GELU, tensorwise, optional: the GELU amax keys of x (the amax
+                               // comes from them instead of `partial`)
     int row_cached;           // row layout with ordinary (cached) stores instead of non-temporal
 };
 
@@ -519,6 +522,39 @@ template <int FMT, int MODE, int ACT>
 __global__ __launch_bounds__(256) void act_cast_kernel(CastArgs a) {
     __shared__ __align__(16) uint32_t tab[act_table_bytes<ACT>() / 4];
     act_table_to_lds(tab, a.act_tab, sizeof(tab));
+    if constexpr (MODE == 0 && ACT == 1) {
+        if (a.gelu_keys) {
+            // the amax of GELU(x) from the keys x's producer wrote: every
+            // workgroup reduces the four key arrays (16 KiB), evaluates GELU
+            // at the values they name from the table in LDS, and the tiles
+            // read that amax as a partials array whose slot 0 holds it
+            __shared__ __align__(16) uint16_t kpart[kMaxAmaxPartials];
+            __shared__ uint32_t kred[kGeluKeyArrays][4];
+            uint32_t k[kGeluKeyArrays];
+#pragma unroll
+            for (int q = 0; q < kGeluKeyArrays; q++) {
+                const uint4 w = reinterpret_cast<const uint4*>(a.gelu_keys + q * kMaxAmaxPartials)[threadIdx.x];
+                k[q] = wave_max_u32(hmax_u16(pkmax_u16(pkmax_u16(w.x, w.y), pkmax_u16(w.z, w.w))));
+            }
+            for (int s = (int)threadIdx.x; s < kMaxAmaxPartials / 8; s += 256)
+                reinterpret_cast<uint4*>(kpart)[s] = make_uint4(0, 0, 0, 0);
+            if ((threadIdx.x & 63) == 0)
+#pragma unroll
+                for (int q = 0; q < kGeluKeyArrays; q++) kred[q][threadIdx.x >> 6] = k[q];
+            __syncthreads();    // also the table copy
+            if (threadIdx.x == 0) {
+#pragma unroll
+                for (int q = 0; q < kGeluKeyArrays; q++) {
+                    uint32_t m = kred[q][0];
+                    for (int w = 1; w < 4; w++) m = m > kred[q][w] ? m : kred[q][w];
+                    k[q] = m;
+                }
+                const uint16_t* t = reinterpret_cast<const uint16_t*>(tab);
+                kpart[0] = (uint16_t)gelu_amax_from_keys(k, [t](uint32_t b) { return gelu_one(b, t); });
+            }
+            a.partial = kpart;
+        }
+    }
     __syncthreads();
     const int64_t ntiles = (a.R >> 7) * (a.C >> 7);
     const int64_t slot0 = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -581,7 +617,8 @@ hipError_t launch_act_quantize(const QuantizeLaunch& q, CastArgs& a, hipStream_t
     hipError_t e = act_tables(stream, t);
     if (e != hipSuccess) return e;
     a.act_tab = q.act == 1 ? static_cast<const void*>(t.gelu) : static_cast<const void*>(t.dgelu);
-    if (q.scaling == 0 && !q.partial_given) {
+    a.gelu_keys = q.gelu_keys;
+    if (q.scaling == 0 && !q.partial_given && !q.gelu_keys) {
         // about two workgroups per CU: each one copies the table to LDS first
         const int64_t n16 = q.rows * q.cols / 8;
         int64_t g = (n16 + (int64_t)kAmaxThreads * 16 - 1) / ((int64_t)kAmaxThreads * 16);
@@ -639,6 +676,7 @@ static CastArgs cast_args(const QuantizeLaunch& q) {
     a.tile_amax = q.partial;
     a.x2 = static_cast<const uint16_t*>(q.x2);
     a.act_tab = nullptr;
+    a.gelu_keys = nullptr;
     a.row_cached = q.rows * q.cols <= (int64_t(128) << 20);
     return a;
 }

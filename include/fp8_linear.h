@@ -281,16 +281,15 @@ fp8_status fp8_gemm_gelu_amax(const void* a, fp8_format format_a, fp8_gemm_scale
 
 /*
  * Tensorwise quantize of GELU(x) (as fp8_quantize_gelu) whose amax comes from
- * the GELU amax partials the producer of x wrote: the cast pass alone (plus
- * one single-workgroup kernel that reads the 16 KiB of keys).  ws: at least
- * fp8_quantize_workspace_bytes(rows, cols, FP8_SCALE_TENSOR) bytes.  The
- * bytes and scales equal fp8_quantize_gelu's on the same x; results are
- * undefined if the partials do not describe x.
+ * the GELU amax partials the producer of x wrote: the cast pass alone (each
+ * of its workgroups reduces the 16 KiB of keys and evaluates GELU at the
+ * values they name), no workspace.  The bytes and scales equal
+ * fp8_quantize_gelu's on the same x; results are undefined if the partials
+ * do not describe x.
  */
 fp8_status fp8_quantize_gelu_from_amax(const void* x_bf16, int64_t rows, int64_t cols, fp8_format format,
                                        unsigned layouts, const fp8_qtensor* out,
-                                       const void* gelu_amax_partials, void* ws, size_t ws_bytes,
-                                       void* stream);
+                                       const void* gelu_amax_partials, void* stream);
 
 /* ---------------------------- weight cache --------------------------- */
 
