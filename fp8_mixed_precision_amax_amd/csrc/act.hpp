@@ -31,8 +31,6 @@ constexpr uint32_t kActLo = 87u << 7;           // magnitude bits of 2^-40
 constexpr uint32_t kActHalf = 44u * 128u;       // entries per sign
 constexpr uint32_t kActEntries = 2u * kActHalf;
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Table indices of the two bf16 halves of w, clamped into the table; far
 // receives the offsets from the table's start, >= kActHalf where a value lies
@@ -99,11 +97,6 @@ __device__ __forceinline__ uint32_t bf16_rne_canon(float v) {
     const uint32_t u = __float_as_uint(v);
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const f32x2_t v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // GELU of the 8 bf16 values of x from the table alone (values outside it

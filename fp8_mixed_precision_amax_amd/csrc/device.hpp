@@ -28,6 +28,17 @@ __device__ __forceinline__ void st_nt8(void* p, uint2 w) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to bf16 (round to nearest even, NaN stays NaN) packed low/high
+// in one dword: a single v_cvt_pk_bf16_f32.  Converting each float on its own
+// and packing with shifts costs four more VALU operations per pair.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

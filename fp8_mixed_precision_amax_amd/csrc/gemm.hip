@@ -34,10 +34,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
             s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
         }
         if (tensorwise) { s.x *= t; s.y *= t; s.z *= t; s.w *= t; }
-        const __bf16 h0 = (__bf16)s.x, h1 = (__bf16)s.y, h2 = (__bf16)s.z, h3 = (__bf16)s.w;
         uint2 w;
-        w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-        w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+        w.x = pack_bf16x2(s.x, s.y);
+        w.y = pack_bf16x2(s.z, s.w);
         reinterpret_cast<uint2*>(c)[i] = w;
         amx = pkmax_u16(amx, pkmax_u16(mag2(w.x), mag2(w.y)));
         if (gelu_keys) {

@@ -228,11 +228,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_kernel(Args g) {
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
                     const int c = (wc * 64 + nj * 32) / 8 + q;
-                    const __bf16 h0 = (__bf16)acc[mi][nj][4 * q], h1 = (__bf16)acc[mi][nj][4 * q + 1];
-                    const __bf16 h2 = (__bf16)acc[mi][nj][4 * q + 2], h3 = (__bf16)acc[mi][nj][4 * q + 3];
                     uint2 w;
-                    w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                    w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                    w.x = pack_bf16x2(acc[mi][nj][4 * q], acc[mi][nj][4 * q + 1]);
+                    w.y = pack_bf16x2(acc[mi][nj][4 * q + 2], acc[mi][nj][4 * q + 3]);
                     *reinterpret_cast<uint2*>(smem + rr * 512 + ((c ^ (rr & 31)) << 4) + 8 * (lane >> 5)) = w;
                 }
             }

@@ -36,6 +36,7 @@
 //    The DMA two stages ahead goes out after the step's first three MFMAs,
 //    not right after the barrier, so the SIMD's two waves leave the barrier
 //    issuing MFMAs (8192 x 8192 x 16384 1.322 -> 1.270 ms).
+#include "device.hpp"
 #include "gemm_common.hpp"
 #include "internal.hpp"
 
@@ -392,12 +393,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_block_kernel(Args g) {
             for (int nj = 0; nj < 2; nj++)
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    const __bf16 h0 = (__bf16)acc[mi][nj][4 * q];
-                    const __bf16 h1 = (__bf16)acc[mi][nj][4 * q + 1];
-                    const __bf16 h2 = (__bf16)acc[mi][nj][4 * q + 2];
-                    const __bf16 h3 = (__bf16)acc[mi][nj][4 * q + 3];
-                    w[mi][nj][q].x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                    w[mi][nj][q].y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
+                    w[mi][nj][q].x = pack_bf16x2(acc[mi][nj][4 * q], acc[mi][nj][4 * q + 1]);
+                    w[mi][nj][q].y = pack_bf16x2(acc[mi][nj][4 * q + 2], acc[mi][nj][4 * q + 3]);
                 }
         const int rw = frow & 7, gw = frow >> 3;          // writer: row in the pass, pass of its row
         const uint32_t wbase = epi_slice + (uint32_t)(rw * 128 + (lane >> 5) * 8);

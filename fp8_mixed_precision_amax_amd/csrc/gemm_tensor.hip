@@ -42,6 +42,8 @@
 //  - epilogue: each wave converts 32 rows at a time to bf16 into a private
 //    4 KiB LDS slice (chunk-major, (row ^ 2 chunk) swizzle: conflict-free
 //    writes and reads) and stores whole 128-byte row segments.
+#include <type_traits>
+
 #include "device.hpp"
 #include "gelu_keys.hpp"
 #include "gemm_common.hpp"
@@ -243,8 +245,13 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
     uint32_t amx = 0;
     GeluKeys gk;   // KEYS: what the quantize of GELU(C) needs instead of an amax pass
 
-    // write one item's accumulators; returns the vector-memory stores issued
-    auto epilogue = [&](const Item& it) __attribute__((always_inline)) -> int {
+    // write one item's accumulators; returns the vector-memory stores issued.
+    // AMAX (a std::bool_constant): fold max |bf16| into amx -- only when the
+    // caller asked for the partials, since it is 4 of the 10 VALU operations
+    // per 4 outputs (131072 x 2048 x 512: a third of the epilogue's VALU).
+    const bool want_amax = g.amax_part != nullptr;
+    auto epilogue = [&](const Item& it, auto amax_on) __attribute__((always_inline)) -> int {
+        constexpr bool AMAX = decltype(amax_on)::value;
         const int64_t i0 = (int64_t)it.ti * BM, j0 = (int64_t)it.tj * BN;
         const int64_t jw = j0 + wj * 64;
         // validity is uniform per wave (I and J are multiples of 128)
@@ -269,14 +276,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
             for (int nj = 0; nj < 2; nj++)
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    const __bf16 h0 = (__bf16)(acc[mi][nj][4 * q] * t_tensor);
-                    const __bf16 h1 = (__bf16)(acc[mi][nj][4 * q + 1] * t_tensor);
-                    const __bf16 h2 = (__bf16)(acc[mi][nj][4 * q + 2] * t_tensor);
-                    const __bf16 h3 = (__bf16)(acc[mi][nj][4 * q + 3] * t_tensor);
                     uint2 w;
-                    w.x = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-                    w.y = (uint32_t)__builtin_bit_cast(uint16_t, h2) | ((uint32_t)__builtin_bit_cast(uint16_t, h3) << 16);
-                    amx = pkmax_u16(amx, pkmax_u16(mag2(w.x), mag2(w.y)));
+                    w.x = pack_bf16x2(acc[mi][nj][4 * q] * t_tensor, acc[mi][nj][4 * q + 1] * t_tensor);
+                    w.y = pack_bf16x2(acc[mi][nj][4 * q + 2] * t_tensor, acc[mi][nj][4 * q + 3] * t_tensor);
+                    if constexpr (AMAX) amx = pkmax_u16(amx, pkmax_u16(mag2(w.x), mag2(w.y)));
                     if constexpr (KEYS) {
                         gk.add(w.x);
                         gk.add(w.y);
@@ -371,7 +374,8 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
         Item n_it;
         const bool more = item_at(g, c_round + 1, n_it);
         const int nstages = c_it.ke - c_it.kb;   // >= 1
-        if (have_prev) st_cur += epilogue(p_it);
+        if (have_prev)
+            st_cur += want_amax ? epilogue(p_it, std::true_type{}) : epilogue(p_it, std::false_type{});
         FP8K_STAGE(true);
         // after the last item the fragments the last half step reads are
         // unused (their stage is a re-read of the last one); reading anyway
@@ -394,7 +398,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_tensor_kernel(Args g) {
                    "+v"(fb1[1])
                  :
                  : "memory");
-    if (have_prev) epilogue(p_it);
+    if (have_prev) {
+        if (want_amax) epilogue(p_it, std::true_type{});
+        else epilogue(p_it, std::false_type{});
+    }
     wait_vm<0>();
     if (g.amax_part) {
         // workgroup max through the (now idle) epilogue slices, one partial
