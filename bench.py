@@ -27,6 +27,7 @@ import csv
 import glob
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -38,6 +39,8 @@ METRIC = "FP8 linear fwd+bwd TFLOP/s incl. quantize at N=131072; quantize GB/s"
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 RIDGE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)      # FLOP per byte
+PEAK_CLOCK_GHZ = 2.4     # the clock the vendor peaks are quoted at
+XCDS = 8                 # accelerator complex dies (one GRBM_GUI_ACTIVE instance each)
 # RTX 4090 fused-layout FP8 medians of the pages (ms): context, not a target
 PAGES_MS = {(512, 2048): 5.4075, (2048, 512): 5.4264}
 
@@ -66,7 +69,7 @@ def parse():
                          "(each with --copy-reference), one line per stage, and exit")
     ap.add_argument("--mfma", metavar="PREFIX",
                     help="matrix-core utilisation of every GEMM launch of a counter run "
-                         "(--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F8), grouped by kernel and shape, and exit")
+                         "(--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_F8 GRBM_GUI_ACTIVE), grouped by kernel and shape, and exit")
     return ap.parse_args()
 
 
@@ -192,7 +195,7 @@ def traffic(fetch_prefix, write_prefix, steps, warmup):
 # other workloads' (N x M x K forward, N x K x M data gradient, M x K x N
 # weight gradient)
 def _bench_gemm_shapes():
-    lin = [(131072, 512, 2048), (131072, 2048, 512), (131072, 512, 8192), (16384, 8192, 8192),
+    lin = [(1024, 512, 512), (131072, 512, 2048), (131072, 2048, 512), (131072, 512, 8192), (16384, 8192, 8192),
            (262144, 512, 8192), (8192, 8192, 16384)]
     out = []
     for N, K, M in lin[:-1]:
@@ -209,13 +212,26 @@ def mfma_summary(prefix, steps, warmup):
     every other GEMM launch grouped by kernel and FLOP count."""
     by = collections.OrderedDict()
     for r in csv.DictReader(open(prefix + "_counter_collection.csv")):
-        d = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d = by.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                  "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     disp = [(kernel_kind(d["name"]), short_name(d["name"]), d) for _, d in sorted(by.items())
             if kernel_kind(d["name"])]
+
+    # GPU clock over a launch: GRBM_GUI_ACTIVE counts the active cycles of
+    # each of the 8 XCDs (the run sums them) over the launch's duration; not
+    # meaningful for launches of a few microseconds (dispatch overhead)
+    def sclk(d):
+        ok = "GRBM_GUI_ACTIVE" in d and d["ns"] >= 20000
+        return d["GRBM_GUI_ACTIVE"] / XCDS / d["ns"] if ok else float("nan")
+
+    def mean(v):
+        return sum(v) / len(v)
+
     used = set()
-    print("| recipe | stage | kernel | MFMA busy % (mean over the timed steps) | FLOP per launch (counter) |")
-    print("|---|---|---|---:|---:|")
+    print("| recipe | stage | kernel | MFMA busy % (mean over the timed steps) | GPU clock GHz | "
+          "busy x clock / 2.4 GHz % | FLOP per launch (counter) |")
+    print("|---|---|---|---:|---:|---:|---:|")
     for recipe in ("tensor", "block"):
         per = collections.OrderedDict()
         for st in walk_steps(disp, steps, warmup, recipe):
@@ -224,8 +240,9 @@ def mfma_summary(prefix, steps, warmup):
                     per.setdefault((stage, name), []).append(d)
                     used.add(id(d))
         for (stage, name), ds in per.items():
-            print("| %s | %s | %s | %.1f | %.4g |" % (recipe, stage, name, sum(x["MfmaUtil"] for x in ds) / len(ds),
-                                                    ds[0]["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512))
+            u, f = mean([x["MfmaUtil"] for x in ds]), mean([sclk(x) for x in ds])
+            print("| %s | %s | %s | %.1f | %.2f | %.1f | %.4g |" % (recipe, stage, name, u, f, u * f / PEAK_CLOCK_GHZ,
+                                                                  ds[0]["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512))
     shapes = _bench_gemm_shapes()
     groups = collections.OrderedDict()
     for kind, name, d in disp:
@@ -234,12 +251,16 @@ def mfma_summary(prefix, steps, warmup):
         flops = d["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512
         match = [sh for sh in shapes if abs(2 * sh[0] * sh[1] * sh[2] - flops) <= 1e-6 * flops]
         tag = "%.4g (%s)" % (flops, ", ".join("%dx%dx%d" % sh for sh in match) if match else "?")
-        groups.setdefault((name, tag), []).append(d["MfmaUtil"])
+        groups.setdefault((name, tag), []).append(d)
     print()
-    print("| kernel | FLOP per launch (GEMMs of the bench with that count, I x J x K) | launches | MFMA busy % mean | min | max |")
-    print("|---|---|---:|---:|---:|---:|")
-    for (name, tag), v in groups.items():
-        print("| %s | %s | %d | %.1f | %.1f | %.1f |" % (name, tag, len(v), sum(v) / len(v), min(v), max(v)))
+    print("| kernel | FLOP per launch (GEMMs of the bench with that count, I x J x K) | launches | MFMA busy % mean | min | max "
+          "| GPU clock GHz mean |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    for (name, tag), ds in groups.items():
+        v = [x["MfmaUtil"] for x in ds]
+        f = mean([sclk(x) for x in ds])
+        print("| %s | %s | %d | %.1f | %.1f | %.1f | %s |" % (name, tag, len(v), mean(v), min(v), max(v),
+                                                            "-" if math.isnan(f) else "%.2f" % f))
 
 
 def summarize(prefix, steps, warmup, recipe="tensor"):
