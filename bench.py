@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -113,16 +114,26 @@ def short_name(name):
             .replace("block::", ""))
 
 
+def _code_only(text):
+    """C/C++ source without its comments and with runs of white space
+    collapsed: edits to comments leave the digest unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest():
-    """sha256 over the HIP/C++ sources and headers of the library."""
+    """sha256 over the code (comments removed) of the library's HIP/C++
+    sources and headers: the profiles record it, and counter figures are used
+    only while it matches."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(ROOT, "fp8_mixed_precision_amax_amd", "csrc", "*")) +
                    glob.glob(os.path.join(ROOT, "include", "*.h")))
     for f in files:
         if f.endswith((".hip", ".hpp", ".cpp", ".h")) and os.path.basename(f) != "ceilings.hip":
             h.update(os.path.basename(f).encode())
-            with open(f, "rb") as fh:
-                h.update(fh.read())
+            with open(f, encoding="utf-8") as fh:
+                h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
@@ -185,7 +196,7 @@ def traffic(fetch_prefix, write_prefix, steps, warmup):
         for stage, b in stage_bytes.items():
             per.setdefault(stage, []).append(b)
     print("# stage  HBM bytes per launch (FETCH_SIZE x %.4f + WRITE_SIZE x %.4f, bytes per counted KiB)  "
-          "library source sha256" % (fr, fw))
+          "library code sha256 (comments stripped)" % (fr, fw))
     digest = source_digest()
     for stage, v in per.items():
         print("%s %d %s" % (stage, round(sum(v) / len(v)), digest))
@@ -324,7 +335,7 @@ def summarize(prefix, steps, warmup, recipe="tensor"):
             out.append("| %s | %s | " % (stage, name) + " | ".join(
                 "%.0f" % (sum(x[k] for x in v) / len(v)) for k in names) + " |")
         out.append("")
-    out.append("library source sha256: %s" % source_digest())
+    out.append("library code sha256 (comments stripped): %s" % source_digest())
     print("\n".join(out))
 
 

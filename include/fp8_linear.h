@@ -3,14 +3,13 @@
  *
  * The library computes the forward and backward pass of a linear layer in
  * FP8 with current scaling, as described in "Native FP8 MLP reconstruction"
- * (rstation.ai, implementation paragraph): a current amax sets each tensor's
- * scale on every call, inputs and weights are cast to E4M3 and incoming
- * gradients to E5M2, one fused cast writes both the ordinary and the
- * transposed layout, the three GEMMs (Y = X W^T, dX = dY W, dW = dY^T X)
- * accumulate in full fp32 precision (no fast accumulation) and write BF16,
- * scales are treated as constants in the backward pass, and the backward
- * pass reuses the forward-rounded X and W while rounding the incoming
- * gradient on its own.  A block-scaled recipe (the Float8BlockScaling recipe
+ * (rstation.ai, implementation paragraph): every tensor's scale is set from
+ * its amax on the call that uses it, X and W are coded as E4M3 and the
+ * gradient dY as E5M2, a single cast pass yields the row-major codes and
+ * their transpose, the three GEMMs (Y = X W^T, dX = dY W, dW = dY^T X) sum
+ * in fp32 (no fast accumulation) and write BF16, and the backward pass
+ * treats the scales as constants, takes the X and W codes of the forward
+ * pass and quantizes dY by itself.  A block-scaled recipe (the Float8BlockScaling recipe
  * of TransformerEngine issue 2852, opening post) quantizes activations and
  * gradients in 1x128 blocks and weights in 128x128 blocks.  A weight cache
  * implements the is_first_microbatch protocol of the same issue (opening

@@ -7,11 +7,12 @@
  *
  * Sources followed (page titles as published):
  *  - "Native FP8 MLP reconstruction" (rstation.ai, general_pretraining post 23),
- *    implementation paragraph: current tensorwise amax scaling, E4M3 for
- *    inputs and weights, E5M2 for incoming gradients, BF16 GEMM outputs,
- *    full-precision accumulation (use_fast_accum=False), a fused cast that
- *    writes ordinary and transposed layouts, detached scales, forward-rounded
- *    X/W reused in backward and the gradient rounded on its own.
+ *    implementation paragraph: every tensor's scale is set from its amax on
+ *    the call that uses it; X and W are coded as E4M3 and dY as E5M2; the
+ *    GEMMs sum in fp32 (no fast accumulation) and write BF16; one cast pass
+ *    yields both the row-major codes and their transpose; the backward pass
+ *    treats the scales as constants, takes the X and W codes of the forward
+ *    pass and quantizes dY by itself.
  *  - "FP8 weight caching shows no speedup (sometimes slowdown) and causes
  *    training curve differences under Float8BlockScaling" (TransformerEngine
  *    issue 2852), opening post and maintainer reply: block-scaled (non-delayed)
