@@ -134,3 +134,54 @@ def test_gemm_deterministic(fp8):
     c2 = fp8.gemm(A, 1, s, B, 0, s)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2)
+
+
+def finite_codes(fmt, shape, rng):
+    """Uniformly random finite codes over the whole format (every binade,
+    subnormals and both signs): NaN (E4M3) or Inf/NaN (E5M2) patterns are
+    moved to the largest finite code of their sign."""
+    b = rng.integers(0, 256, int(np.prod(shape)), dtype=np.uint8)
+    if fmt == "e4m3":
+        b[(b & 0x7F) == 0x7F] -= 1
+    else:
+        b[(b & 0x7C) == 0x7C] &= 0xFB
+    return b.reshape(shape)
+
+
+KMAX = (1 << 23) - 128   # the longest contraction the library accepts
+
+
+@pytest.mark.parametrize("scaling", ["tensor", "block", "block_wide"])
+def test_gemm_longest_contraction(fp8, scaling):
+    """K = 2^23 - 128 (one 128 x 128 output tile, the most split-K slices),
+    operands drawn over every finite code: sampled outputs against the oracle
+    and the matrix-core emulation.  Offsets inside a tile reach ~2^31 bytes
+    here, the edge of the 32-bit buffer offsets the kernels use."""
+    I = J = 128
+    print("longest contraction", scaling, I, J, KMAX, flush=True)
+    rng = np.random.default_rng(23)
+    A = finite_codes("e5m2", (I, KMAX), rng)
+    B = finite_codes("e4m3", (J, KMAX), rng)
+    ii = rng.integers(0, I, 16)
+    jj = rng.integers(0, J, 16)
+    if scaling == "tensor":
+        sa, sb = np.float32(2.0 ** -17), np.float32(3.0e-6)
+        c = fp8.gemm(dev(A), 1, fp8.gemm_scale(torch.tensor([sa], device="cuda")), dev(B), 0,
+                     fp8.gemm_scale(torch.tensor([sb], device="cuda")))
+        torch.cuda.synchronize()
+        ref = oracle.gemm_tensor_sampled(A, "e5m2", B, "e4m3", sa, sb, ii, jj)
+        t = np.float32(sa * sb)
+    else:
+        # per-row factors on both operands (the weight gradient's kernel), or
+        # one factor per 128 rows of B (a 128x128-block weight: the wide kernel)
+        KB = KMAX // 128
+        gb = 1 if scaling == "block" else 128
+        tA = rng.uniform(1e-6, 1e-5, (I, KB)).astype(np.float32)
+        tB = rng.uniform(1e-6, 1e-5, (J // gb, KB)).astype(np.float32)
+        sA, sB = oracle.BlockScale(tA, 1, KB, 1), oracle.BlockScale(tB, gb, KB, 1)
+        c = fp8.gemm(dev(A), 1, fp8.gemm_scale(dev(tA), 1, KB, 1), dev(B), 0, fp8.gemm_scale(dev(tB), gb, KB, 1))
+        torch.cuda.synchronize()
+        ref = oracle.gemm_block_sampled(A, "e5m2", sA, B, "e4m3", sB, ii, jj)
+        t = (tA, np.repeat(tB, gb, axis=0))
+    got = to_np_u16(c)[ii, jj]
+    print(check_gemm(got, ref, A, "e5m2", B, "e4m3", t, KMAX, "gemm K=2^23-128 " + scaling, ii, jj), flush=True)
