@@ -623,7 +623,7 @@ def ceilings(fp8, torch, synth, dev):
 
     res = {"hbm_buffer_bytes": nbytes}
     res["hbm_read_gbs"] = max(best(lambda g, v=v: cl.fp8c_hbm_read(v, g, x.data_ptr(), n16, o.data_ptr(), st), nbytes)
-                              for v in (0, 1))
+                              for v in (0, 1, 2))
     res["hbm_write_gbs"] = max(best(lambda g, v=v: cl.fp8c_hbm_write(v, g, y.data_ptr(), n16, st), nbytes)
                                for v in (0, 1))
     res["hbm_copy_gbs"] = best(lambda g: cl.fp8c_hbm_copy(g, x.data_ptr(), y.data_ptr(), n16, st), 2 * nbytes)

@@ -83,12 +83,13 @@ __global__ __launch_bounds__(512) void mfma_kernel(int iters, float* out, unsign
 }  // namespace
 
 // variant 0: one ordinary load per thread per step; 1: four non-temporal
-// loads in flight.  out: 4 bytes of device memory.
+// loads in flight; 2: one non-temporal load.  out: 4 bytes of device memory.
 extern "C" int fp8c_hbm_read(int variant, int grid, const void* x, int64_t n16, void* out, hipStream_t st) {
     const u4* p = static_cast<const u4*>(x);
     uint32_t* o = static_cast<uint32_t*>(out);
     if (variant == 0) hipLaunchKernelGGL((read_kernel<1, false>), dim3(grid), dim3(256), 0, st, p, n16, o);
-    else hipLaunchKernelGGL((read_kernel<4, true>), dim3(grid), dim3(256), 0, st, p, n16, o);
+    else if (variant == 1) hipLaunchKernelGGL((read_kernel<4, true>), dim3(grid), dim3(256), 0, st, p, n16, o);
+    else hipLaunchKernelGGL((read_kernel<1, true>), dim3(grid), dim3(256), 0, st, p, n16, o);
     return (int)hipGetLastError();
 }
 

@@ -78,30 +78,26 @@ __device__ __forceinline__ uint32_t mag8_max(uint32_t m, uint4 v) {
     return pkmax_u16(m, pkmax_u16(pkmax_u16(mag2(v.x), mag2(v.y)), pkmax_u16(mag2(v.z), mag2(v.w))));
 }
 
-// One sweep of the tensor from front to back (grid-stride).  A tensor that
-// fits the memory-side cache is read with ordinary loads, one 16-byte load
-// per thread per step, so the cast that follows (last tile first) finds the
+// One sweep of the tensor from front to back (grid-stride, one 16-byte load
+// per thread per step).  A tensor that fits the memory-side cache is read
+// with ordinary loads, so the cast that follows (last tile first) finds the
 // most recently read data still cached.  A larger one cannot stay cached
 // (the cast gains nothing from the cache: measured) and is streamed with
-// four non-temporal loads in flight per thread: with one, the grid keeps
-// about 8 MiB of reads outstanding, half of what HBM's latency needs.
+// non-temporal loads, which also spare the cache's dirty lines (left by the
+// kernel before) the write-back an allocating read would force: after a
+// 512 MiB write, ordinary loads read at 3.2-3.6 TB/s and non-temporal ones at
+// 6.2-6.9 TB/s.  One load in flight per thread (2048 x 1024 threads: 32 MiB
+// outstanding, all within one contiguous window of the tensor) measured
+// faster than four spaced a grid stride apart: 131072 x 2048 quantize
+// 294.5 -> 284.3 us, 262144 x 2048 596 -> 574 us.
 // The packed magnitude maximum of this thread's share of x when `nblocks`
 // workgroups sweep it and this one is number `block`.
 template <bool STREAM>
 __device__ __forceinline__ uint32_t amax_sweep(const uint4* __restrict__ x, int64_t n16, int block, int nblocks) {
     uint32_t m = 0;
     const int64_t stride = (int64_t)nblocks * blockDim.x;
-    int64_t i = (int64_t)block * blockDim.x + threadIdx.x;
-    if constexpr (STREAM) {
-        for (; i + 3 * stride < n16; i += 4 * stride) {
-            uint4 v[4];
-#pragma unroll
-            for (int k = 0; k < 4; k++) v[k] = ld_nt16(x + i + k * stride);
-#pragma unroll
-            for (int k = 0; k < 4; k++) m = mag8_max(m, v[k]);
-        }
-    }
-    for (; i < n16; i += stride) m = mag8_max(m, x[i]);
+    for (int64_t i = (int64_t)block * blockDim.x + threadIdx.x; i < n16; i += stride)
+        m = mag8_max(m, STREAM ? ld_nt16(x + i) : x[i]);
     return m;
 }
 
@@ -130,9 +126,10 @@ __global__ __launch_bounds__(kAmaxStreamThreads) void amax_pair_kernel(const uin
 template <int ACT> constexpr uint32_t act_table_bytes() { return ACT == 2 ? kActEntries * 4 : kActEntries * 2; }
 
 // amax of GELU(x) (ACT 1) or of dGELU(x, x2) (ACT 2): the transform is
-// applied as in the cast, so both passes see the same bf16 values.  Four
-// loads in flight per thread; non-temporal ones (STREAM) for inputs larger
-// than the memory-side cache, as in amax_partial_kernel.
+// applied as in the cast, so both passes see the same bf16 values.  One
+// load per input in flight per thread (as amax_sweep; four spaced a grid
+// stride apart measured 4-5 us slower on 131072 x 2048); non-temporal ones
+// (STREAM) for inputs larger than the memory-side cache.
 template <int ACT, bool STREAM>
 __device__ __forceinline__ uint4 amax_ld(const uint4* p) {
     if constexpr (STREAM) return ld_nt16(p);
@@ -149,22 +146,10 @@ __global__ __launch_bounds__(kAmaxStreamThreads) void act_amax_kernel(const uint
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        uint4 v[4], u[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            v[k] = amax_ld<ACT, STREAM>(x + i + k * stride);
-            if constexpr (ACT == 2) u[k] = amax_ld<ACT, STREAM>(x2 + i + k * stride);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; k++)
-            m = mag8_max(m, ACT == 1 ? gelu8(v[k], reinterpret_cast<const uint16_t*>(tab))
-                                     : dgelu8(v[k], u[k], reinterpret_cast<const float*>(tab)));
-    }
     for (; i < n16; i += stride) {
-        const uint4 v = x[i];
-        m = mag8_max(m, ACT == 1 ? gelu8(v, reinterpret_cast<const uint16_t*>(tab))
-                                 : dgelu8(v, x2[i], reinterpret_cast<const float*>(tab)));
+        const uint4 v = amax_ld<ACT, STREAM>(x + i);
+        if constexpr (ACT == 1) m = mag8_max(m, gelu8(v, reinterpret_cast<const uint16_t*>(tab)));
+        else m = mag8_max(m, dgelu8(v, amax_ld<ACT, STREAM>(x2 + i), reinterpret_cast<const float*>(tab)));
     }
     amax_store_partial(m, partial);
 }
