@@ -15,12 +15,6 @@
 
 namespace fp8k {
 
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 ld_nt_f4(const float* p) {
-    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-    return make_float4(v.x, v.y, v.z, v.w);
-}
-
 // Sum split-K partials in split order, apply the tensorwise factor, bf16.
 // With amax_part, also one partial max |bf16 C| per block (block 0 zeroes the
 // slots no block owns); with gelu_keys, the four GELU amax keys of C per
@@ -34,20 +28,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     uint32_t amx = 0;
     GeluKeys gk;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
-        // non-temporal loads, eight slices in flight, added in split order
-        // (2048 x 512 x 131072 with its reduce 141.5 -> 138.5 us; the batching
-        // alone with ordinary loads measured no faster)
-        float4 s = ld_nt_f4(part + 4 * i);
-        int z = 1;
-        for (; z + 7 < splits; z += 8) {
-            float4 p[8];
-#pragma unroll
-            for (int k = 0; k < 8; k++) p[k] = ld_nt_f4(part + (int64_t)(z + k) * IJ + 4 * i);
-#pragma unroll
-            for (int k = 0; k < 8; k++) { s.x += p[k].x; s.y += p[k].y; s.z += p[k].z; s.w += p[k].w; }
-        }
-        for (; z < splits; z++) {
-            const float4 p = ld_nt_f4(part + (int64_t)z * IJ + 4 * i);
+        float4 s = reinterpret_cast<const float4*>(part)[i];
+        for (int z = 1; z < splits; z++) {
+            const float4 p = reinterpret_cast<const float4*>(part + (int64_t)z * IJ)[i];
             s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
         }
         if (tensorwise) { s.x *= t; s.y *= t; s.z *= t; s.w *= t; }
