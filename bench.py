@@ -472,11 +472,6 @@ def config_times(fp8, torch, synth, steps, warmup, reps, dev):
     return out
 
 
-def _gelu_ref(torch, a):
-    x = a.float()
-    return (0.5 * x * (1.0 + torch.erf(x * 0.7071067811865476))).to(torch.bfloat16)
-
-
 def mlp_stack_times(fp8, torch, synth, N, cycles, dev, recipe="tensor", layers=8, mbs=4):
     """The MLP stack of the gradient-accumulation workload: `layers` blocks of
     512 -> 2048 (GELU) -> 512, `mbs` microbatches of N tokens per cycle, the

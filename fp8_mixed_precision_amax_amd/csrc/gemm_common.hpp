@@ -80,39 +80,6 @@ __device__ __forceinline__ v8i ds_frag(uint32_t a0, uint32_t a1) {
     return __builtin_bit_cast(v8i, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Six 32-byte fragments (A rows at a0/a1 + 0, 4096, 8192, 12288; B rows at
-// b0/b1 + 0, 4096) read and waited for in ONE asm statement: the outputs
-// exist only once the data has landed, so the compiler cannot copy a
-// register whose load is still in flight.
-__device__ __forceinline__ void ds_frags6_wait(v8i (&fa)[4], v8i (&fb)[2], uint32_t a0, uint32_t a1, uint32_t b0,
-                                               uint32_t b1) {
-    u32x4 x0, x1, x2, x3, x4, x5, x6, x7, y0, y1, y2, y3;
-    asm volatile(
-        "ds_read_b128 %0, %12 offset:0\n\t"
-        "ds_read_b128 %1, %13 offset:0\n\t"
-        "ds_read_b128 %2, %12 offset:4096\n\t"
-        "ds_read_b128 %3, %13 offset:4096\n\t"
-        "ds_read_b128 %4, %12 offset:8192\n\t"
-        "ds_read_b128 %5, %13 offset:8192\n\t"
-        "ds_read_b128 %6, %12 offset:12288\n\t"
-        "ds_read_b128 %7, %13 offset:12288\n\t"
-        "ds_read_b128 %8, %14 offset:0\n\t"
-        "ds_read_b128 %9, %15 offset:0\n\t"
-        "ds_read_b128 %10, %14 offset:4096\n\t"
-        "ds_read_b128 %11, %15 offset:4096\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(x4), "=&v"(x5), "=&v"(x6), "=&v"(x7), "=&v"(y0),
-          "=&v"(y1), "=&v"(y2), "=&v"(y3)
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
-        : "memory");
-    fa[0] = __builtin_bit_cast(v8i, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-    fa[1] = __builtin_bit_cast(v8i, __builtin_shufflevector(x2, x3, 0, 1, 2, 3, 4, 5, 6, 7));
-    fa[2] = __builtin_bit_cast(v8i, __builtin_shufflevector(x4, x5, 0, 1, 2, 3, 4, 5, 6, 7));
-    fa[3] = __builtin_bit_cast(v8i, __builtin_shufflevector(x6, x7, 0, 1, 2, 3, 4, 5, 6, 7));
-    fb[0] = __builtin_bit_cast(v8i, __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7));
-    fb[1] = __builtin_bit_cast(v8i, __builtin_shufflevector(y2, y3, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 // Buffer resource over `bytes` bytes at `base` (raw, stride 0): reads at
 // offsets >= bytes return zero instead of touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {

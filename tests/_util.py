@@ -188,11 +188,6 @@ def mfma_model(A, fa, B, fb, t, ii=None, jj=None, anchor=None):
     return emu, hw
 
 
-def mfma_window_bound(A, fa, B, fb, t, ii=None, jj=None):
-    """hw alone (see the module docstring)."""
-    return mfma_model(A, fa, B, fb, t, ii, jj)[1]
-
-
 def check_bf16(got_bits, ref_bits, Kc, name="", hw=None, emu_bits=None):
     """Assert the BF16 tolerance against the oracle (and, with emu_bits,
     against the matrix-core emulation); return a small report dict."""
