@@ -259,3 +259,26 @@ def test_noalloc_forward_rejections(L):
     assert call(256, 512, 512, recipe=5) == ENUM
     assert call(256, 8192, 8192) == WORKSPACE
     assert b"8388608-byte device scratch" in L.fp8_last_error()
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library the package raises on first use; nothing
+    falls back to a CPU path (run in a fresh interpreter whose package points
+    at an empty directory)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from fp8_mixed_precision_amax_amd import _lib\n"
+        "import fp8_mixed_precision_amax_amd as fp8\n"
+        "_lib.LIB_PATH = %r\n"
+        "_lib._lib = None\n"
+        "try:\n"
+        "    fp8.lib()\n"
+        "except ImportError as e:\n"
+        "    print('raised:', e)\n"
+        "    sys.exit(0)\n"
+        "sys.exit(1)\n" % (ROOT, str(tmp_path / "libfp8linear.so")))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "not built" in r.stdout
