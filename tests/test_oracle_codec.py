@@ -74,7 +74,8 @@ def brute_force_encode(v, fmt):
     order = np.argsort(vals, kind="stable")
     finite, vals = finite[order], vals[order]
     v = np.asarray(v, np.float32)
-    vd = v.astype(np.float64)
+    with np.errstate(invalid="ignore"):   # NaN patterns among the inputs
+        vd = v.astype(np.float64)
     out = np.empty(v.shape, np.uint8)
     flat_v = vd.reshape(-1)
     flat_o = out.reshape(-1)
@@ -138,7 +139,8 @@ def test_encode_matches_torch_cast_in_range(fmt):
     rng = np.random.default_rng(99)
     v = structured_fp32(fmt, rng)
     lim = 464.0 if fmt == "e4m3" else 61440.0
-    keep = np.isfinite(v) & (np.abs(v.astype(np.float64)) < lim)
+    with np.errstate(invalid="ignore"):   # NaN patterns among the inputs
+        keep = np.isfinite(v) & (np.abs(v.astype(np.float64)) < lim)
     v = v[keep]
     mine = oracle.enc(v, fmt)
     ref = torch.from_numpy(v).to(TORCH_DT[fmt]).view(torch.uint8).numpy()
